@@ -1,0 +1,46 @@
+"""fp64 CPU oracle for the DiT self-attention path (test infrastructure).
+
+This package is test infrastructure, not product code. Only the test suite,
+the package smoke check and the benchmark's CPU-baseline leg may import it.
+It shares no code with the HIP library: it is a plain NumPy float64
+restatement of what the path computes, written from the pages' definitions.
+
+What each function follows (pages are cited by title and section):
+  * rope_tables / rope_split_halves / rope_interleaved /
+    interleaved_to_split_permutation -- Difflet PR #153 "TPU sequence
+    parallelism ...", the FLUX split-RoPE commit (channels permuted once to
+    [0, 2, ..., 1, 3, ...] so the pairwise rotation becomes a slice and a
+    concat; q.k is unchanged when both get the same permutation) and the Wan
+    padding + split RoPE commit (pad rows get the identity rotation). The
+    per-axis frequency schedule is not printed on the pages; the plain
+    reading used here is the standard 1-D schedule theta^(-2j/c_a) per axis
+    over that axis's own channel count, axes concatenated in pair space.
+  * attention -- softmax(scale * Q K^T) V over the valid keys only, with the
+    natural-log log-sum-exp per query row (mstar PR #376, "Ragged attention
+    returns the log-sum-exp": fp32, natural log). Pad keys are dropped
+    exactly (Difflet PR #153, Wan padding commit; maxdiffusion PR #491, the
+    ragged KV tail carries the real length). Pad query rows give O = 0 and
+    LSE = -inf (a convention: -inf is the merge's identity).
+  * lse_merge -- combining per-key-shard (O, LSE) pairs into the single-pass
+    result (mstar PR #376, attention_over_sharded_keys).
+  * pad_tokens / unpad_tokens / plan_padding -- tail padding of token rows to
+    a multiple (Difflet PR #153 Wan padding commit, 4680 -> 4736;
+    maxdiffusion PR #491 lane padding, 75,600 -> 75,776 at CP=4).
+  * attention_bruteforce -- the same definition in pure-Python loops for
+    tiny sizes, used only to cross-check `attention`.
+"""
+from .reference import (  # noqa: F401
+    bf16_to_f64,
+    plan_padding,
+    pad_tokens,
+    unpad_tokens,
+    rope_pair_frequencies,
+    rope_tables,
+    rope_split_halves,
+    rope_interleaved,
+    interleaved_to_split_permutation,
+    attention,
+    attention_bruteforce,
+    lse_merge,
+    dit_path,
+)

@@ -1,0 +1,372 @@
+"""Pins for the fp64 oracle: closed forms, invariants, library routines,
+brute force, the pages' printed padding plans, and negative controls that
+plant a plausible mistake in an oracle function and show a pin catches it.
+
+All of these run on the CPU (no GPU marker).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import reference as R
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ inputs
+def test_bf16_rounding_matches_torch_on_every_pattern():
+    # Every finite bf16 pattern survives f32 widening and re-rounding, and
+    # torch's own RNE conversion agrees with the generator's on all of them.
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = W.bf16_bits_to_f32(bits)
+    finite = np.isfinite(f)
+    ours = W.bf16_bits(f[finite])
+    assert np.array_equal(ours, bits[finite])
+    t = torch.from_numpy(f[finite].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, t)
+
+
+def test_bf16_rounding_matches_torch_on_random_and_tie_values():
+    r = rng(1)
+    x = np.concatenate([
+        r.standard_normal(200000).astype(np.float32) * np.float32(10.0) ** r.integers(-30, 30, 200000).astype(np.float32),
+        # exact ties: low 16 bits == 0x8000, both parities of the kept lsb
+        (r.integers(0, 1 << 15, 50000, dtype=np.uint32) << 17 | 0x8000).view(np.float32),
+        (r.integers(0, 1 << 15, 50000, dtype=np.uint32) << 17 | 0x18000).view(np.float32),
+    ]).astype(np.float32)
+    x = x[np.isfinite(x)]
+    t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(W.bf16_bits(x), t)
+
+
+def test_oracle_widening_is_exact():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    a = oracle.bf16_to_f64(bits)
+    b = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (a == b) | (np.isnan(a) & np.isnan(b))
+    assert same.all()
+
+
+def test_garbage_is_finite_and_uses_the_whole_range():
+    g = W.finite_garbage_bits(rng(2), (4096, 64))
+    f = W.bf16_bits_to_f32(g)
+    assert np.isfinite(f).all()
+    assert np.abs(f).max() > 1e30 and (f < 0).any() and (f > 0).any()
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_token_counts(name):
+    w = W.WORKLOADS[name]
+    assert int(np.prod(w.grid)) + w.n_text == w.s_valid
+    assert sum(w.axes) == w.d and all(c % 2 == 0 for c in w.axes)
+    assert w.s_pad >= w.s_valid and oracle.plan_padding(w.s_valid, 128 if w.d == 128 else 64) == w.s_pad
+    pos = W.positions(w)
+    assert pos.shape == (w.s_pad, len(w.axes))
+    n_grid = int(np.prod(w.grid))
+    assert (pos[n_grid:] == 0).all()
+    assert tuple(pos[:n_grid].max(axis=0) + 1) == w.grid
+
+
+def test_generator_is_deterministic_against_stored_hashes():
+    import hashlib
+    with open(os.path.join(GOLDEN, "input_hashes.json")) as fh:
+        stored = json.load(fh)["hashes"]
+    for key, want in stored.items():
+        name, heads = key.split(":")
+        w = W.WORKLOADS[name]
+        hs = None if heads == "all" else [int(heads)]
+        q, k, v = W.make_qkv(w, heads=hs)
+        got = hashlib.sha256(q.tobytes() + k.tobytes() + v.tobytes()).hexdigest()
+        assert got == want, key
+
+
+# ------------------------------------------------------------------ padding
+def test_padding_plans_printed_on_the_pages():
+    with open(os.path.join(GOLDEN, "padding_plans.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        assert oracle.plan_padding(c["s_valid"], c["multiple"]) == c["s_pad"], c["cite"]
+
+
+def test_pad_unpad_round_trip_and_zero_fill():
+    x = rng(3).standard_normal((2, 37, 5, 8))
+    p = oracle.pad_tokens(x, 48)
+    assert p.shape == (2, 48, 5, 8)
+    assert (p[:, 37:] == 0).all() and np.array_equal(p[:, :37], x)
+    assert np.array_equal(oracle.unpad_tokens(p, 37), x)
+
+
+# ------------------------------------------------------------------ RoPE
+def test_rope_frequencies_closed_form():
+    # theta = 16, axes of 4 and 8 channels:
+    #   axis 0: 16^(-0/4), 16^(-2/4) = 1, 1/4
+    #   axis 1: 16^(-2j/8) = 2^(-j): 1, 1/2, 1/4, 1/8
+    f = oracle.rope_pair_frequencies((4, 8), 16.0)
+    assert np.allclose(f, [1.0, 0.25, 1.0, 0.5, 0.25, 0.125], rtol=0, atol=1e-15)
+    # the standard 1-D schedule at theta=10000, d=64: last pair 10000^(-62/64)
+    f = oracle.rope_pair_frequencies((64,), 10000.0)
+    assert f[0] == 1.0 and abs(f[31] - 10000.0 ** (-62 / 64)) < 1e-18
+
+
+def test_rope_tables_closed_form_values():
+    pos = np.array([[0, 0], [3, 5], [7, 2]])
+    c, s = oracle.rope_tables(pos, (4, 8), 16.0)
+    freqs = [1.0, 0.25, 1.0, 0.5, 0.25, 0.125]
+    axis = [0, 0, 1, 1, 1, 1]
+    for i in range(3):
+        for j in range(6):
+            ang = pos[i, axis[j]] * freqs[j]
+            assert abs(c[i, j] - math.cos(ang)) < 1e-15
+            assert abs(s[i, j] - math.sin(ang)) < 1e-15
+    assert (c[0] == 1).all() and (s[0] == 0).all()
+
+
+def test_rope_interleaved_is_complex_multiplication():
+    r = rng(4)
+    d, S = 16, 9
+    y = r.standard_normal((S, d))
+    pos = r.integers(0, 50, (S, 2))
+    c, s = oracle.rope_tables(pos, (6, 10), 10000.0)
+    ang = np.arctan2(s, c)
+    z = (y[:, 0::2] + 1j * y[:, 1::2]) * np.exp(1j * ang)
+    out = oracle.rope_interleaved(y, c, s)
+    assert np.allclose(out[:, 0::2], z.real, atol=1e-13)
+    assert np.allclose(out[:, 1::2], z.imag, atol=1e-13)
+
+
+def test_split_halves_equals_interleaved_after_permutation():
+    r = rng(5)
+    for d in (8, 64, 128):
+        x = r.standard_normal((3, 11, d))
+        pos = r.integers(0, 100, (11, 1))
+        c, s = oracle.rope_tables(pos, (d,), 10000.0)
+        P = oracle.interleaved_to_split_permutation(d)
+        a = oracle.rope_split_halves(x[..., P], c, s)
+        b = oracle.rope_interleaved(x, c, s)[..., P]
+        assert np.array_equal(a, b)
+
+
+def test_rope_preserves_norm_and_position_zero_is_identity():
+    r = rng(6)
+    x = r.standard_normal((5, 20, 128)) * 3
+    pos = r.integers(0, 80, (20, 3))
+    c, s = oracle.rope_tables(pos, (44, 42, 42), 10000.0)
+    y = oracle.rope_split_halves(x, c, s)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    c0, s0 = oracle.rope_tables(np.zeros((20, 3), int), (44, 42, 42), 10000.0)
+    assert np.array_equal(oracle.rope_split_halves(x, c0, s0), x)
+
+
+def test_rope_relative_position_property():
+    r = rng(7)
+    axes = (44, 42, 42)
+    q = r.standard_normal(128)
+    k = r.standard_normal(128)
+    p = np.array([[1, 4, 9]])
+    pk = np.array([[2, 11, 3]])
+    delta = np.array([[5, -3, 17]])
+
+    def rot(x, pos):
+        c, s = oracle.rope_tables(pos, axes, 10000.0)
+        return oracle.rope_split_halves(x[None], c, s)[0]
+
+    a = rot(q, p) @ rot(k, pk)
+    b = rot(q, p + delta) @ rot(k, pk + delta)
+    assert abs(a - b) < 1e-12 * (1 + abs(a))
+
+
+# ------------------------------------------------------------------ attention
+def rand_qkv(seed, B, H, Sq, Skv, d, scale=1.0):
+    r = rng(seed)
+    return (r.standard_normal((B, H, Sq, d)) * scale, r.standard_normal((B, H, Skv, d)),
+            r.standard_normal((B, H, Skv, d)))
+
+
+def test_softmax_weights_sum_to_one():
+    q, k, v = rand_qkv(8, 1, 2, 33, 70, 64, scale=2.0)
+    O, L = oracle.attention(q, k, v, q_valid=33, kv_valid=61)
+    s = np.einsum("bhid,bhjd->bhij", q, k[:, :, :61]) / 8.0
+    P = np.exp(s - L[..., None])
+    assert np.allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert np.allclose(np.einsum("bhij,bhjd->bhid", P, v[:, :, :61]), O, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_valid", [1, 7, 64, 300])
+def test_zero_query_gives_mean_of_valid_values(kv_valid):
+    _, k, v = rand_qkv(9, 1, 2, 5, 320, 64)
+    q = np.zeros((1, 2, 5, 64))
+    O, L = oracle.attention(q, k, v, q_valid=5, kv_valid=kv_valid)
+    assert np.allclose(O, v[:, :, :kv_valid].mean(axis=2, keepdims=True), atol=1e-13)
+    assert np.allclose(L, math.log(kv_valid), rtol=0, atol=1e-13)
+
+
+def test_single_valid_key_gives_its_value_and_score():
+    q, k, v = rand_qkv(10, 1, 1, 4, 16, 128)
+    O, L = oracle.attention(q, k, v, q_valid=4, kv_valid=1)
+    assert np.allclose(O, np.broadcast_to(v[:, :, :1], O.shape), atol=1e-14)
+    assert np.allclose(L[0, 0], (q[0, 0] @ k[0, 0, 0]) / math.sqrt(128), atol=1e-13)
+
+
+def test_two_key_worked_example():
+    # q = a*e0, k0 = e0, k1 = -e0 -> s0 = a/sqrt(d), s1 = -s0
+    d, a = 64, 3.0
+    q = np.zeros((1, 1, 1, d)); q[..., 0] = a
+    k = np.zeros((1, 1, 2, d)); k[0, 0, 0, 0] = 1; k[0, 0, 1, 0] = -1
+    v = np.zeros((1, 1, 2, d)); v[0, 0, 0, :] = 1.0; v[0, 0, 1, :] = -2.0
+    s0 = a / 8.0
+    w0 = 1.0 / (1.0 + math.exp(-2 * s0))
+    O, L = oracle.attention(q, k, v, 1, 2)
+    assert np.allclose(O[0, 0, 0], w0 * 1.0 + (1 - w0) * -2.0, atol=1e-15)
+    assert abs(L[0, 0, 0] - (s0 + math.log1p(math.exp(-2 * s0)))) < 1e-15
+
+
+def test_lse_against_scipy_logsumexp():
+    q, k, v = rand_qkv(11, 2, 3, 40, 90, 128, scale=4.0)
+    O, L = oracle.attention(q, k, v, q_valid=40, kv_valid=77, scale=0.3)
+    s = np.einsum("bhid,bhjd->bhij", q, k[:, :, :77]) * 0.3
+    assert np.allclose(L, scipy.special.logsumexp(s, axis=-1), atol=1e-12)
+
+
+def test_pad_rows_are_excluded_exactly():
+    q, k, v = rand_qkv(12, 1, 2, 64, 64, 64)
+    O1, L1 = oracle.attention(q, k, v, q_valid=50, kv_valid=45)
+    g = W.bf16_bits_to_f32(W.finite_garbage_bits(rng(13), (1, 2, 19, 64))).astype(np.float64)
+    k2, v2, q2 = k.copy(), v.copy(), q.copy()
+    k2[:, :, 45:] = g; v2[:, :, 45:] = g[..., ::-1]; q2[:, :, 50:] = g[:, :, :14]
+    O2, L2 = oracle.attention(q2, k2, v2, q_valid=50, kv_valid=45)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    assert (O1[:, :, 50:] == 0).all() and np.isneginf(L1[:, :, 50:]).all()
+
+
+def test_no_valid_keys_gives_zero_and_minus_inf():
+    q, k, v = rand_qkv(14, 1, 1, 8, 8, 64)
+    O, L = oracle.attention(q, k, v, q_valid=8, kv_valid=0)
+    assert (O == 0).all() and np.isneginf(L).all()
+
+
+@pytest.mark.parametrize("Sq,Skv,d,qv,kv", [(5, 9, 4, 5, 9), (16, 16, 8, 13, 11), (7, 3, 6, 7, 1), (12, 16, 16, 12, 16)])
+def test_bruteforce_agrees(Sq, Skv, d, qv, kv):
+    q, k, v = rand_qkv(15 + d, 1, 2, Sq, Skv, d, scale=1.5)
+    O1, L1 = oracle.attention(q, k, v, qv, kv)
+    O2, L2 = oracle.attention_bruteforce(q, k, v, qv, kv)
+    assert np.allclose(O1, O2, rtol=0, atol=1e-12)
+    fin = np.isfinite(L2)
+    assert np.array_equal(np.isfinite(L1), fin)
+    assert np.allclose(L1[fin], L2[fin], rtol=0, atol=1e-12)
+
+
+def test_row_subset_matches_full_evaluation():
+    q, k, v = rand_qkv(16, 1, 2, 100, 120, 64)
+    rows = np.array([0, 3, 50, 98, 99])
+    Of, Lf = oracle.attention(q, k, v, 97, 111)
+    Or, Lr = oracle.attention(q, k, v, 97, 111, rows=rows)
+    assert np.allclose(Or, Of[:, :, rows], rtol=0, atol=1e-14)
+    assert np.array_equal(np.isneginf(Lr), np.isneginf(Lf[:, :, rows]))
+    f = np.isfinite(Lr)
+    assert np.allclose(Lr[f], Lf[:, :, rows][f], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------ merge
+def _shards(q, k, v, cuts, q_valid, total_valid):
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        kv_valid = max(0, min(total_valid - a, b - a))
+        parts.append(oracle.attention(q, k[:, :, a:b], v[:, :, a:b], q_valid, kv_valid))
+    return parts
+
+
+@pytest.mark.parametrize("cuts", [[0, 64, 128], [0, 10, 10, 77, 128], [0, 128], [0, 100, 120, 128]])
+def test_merge_of_key_shards_equals_single_pass(cuts):
+    q, k, v = rand_qkv(17, 1, 2, 40, 128, 64, scale=2.0)
+    O, L = oracle.attention(q, k, v, 37, 110)
+    parts = _shards(q, k, v, cuts, 37, 110)
+    Om, Lm = oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts], q_valid=37)
+    assert np.allclose(Om, O, rtol=0, atol=1e-12)
+    assert np.array_equal(np.isneginf(Lm), np.isneginf(L))
+    f = np.isfinite(L)
+    assert np.allclose(Lm[f], L[f], rtol=1e-13, atol=0)
+
+
+def test_merge_lse_is_logaddexp():
+    r = rng(18)
+    L1, L2 = r.standard_normal((3, 7)) * 5, r.standard_normal((3, 7)) * 5
+    O1, O2 = r.standard_normal((3, 7, 4)), r.standard_normal((3, 7, 4))
+    O, L = oracle.lse_merge([O1, O2], [L1, L2])
+    assert np.allclose(L, np.logaddexp(L1, L2), atol=1e-13)
+    w1 = scipy.special.expit(L1 - L2)
+    assert np.allclose(O, w1[..., None] * O1 + (1 - w1)[..., None] * O2, atol=1e-13)
+
+
+def test_merge_all_empty_and_identity():
+    O1 = rng(19).standard_normal((2, 5, 4))
+    L1 = rng(20).standard_normal((2, 5))
+    O, L = oracle.lse_merge([O1], [L1])
+    assert np.allclose(O, O1, atol=1e-15) and np.allclose(L, L1, atol=1e-15)
+    ninf = np.full((2, 5), -np.inf)
+    O, L = oracle.lse_merge([O1, O1], [ninf, ninf])
+    assert (O == 0).all() and np.isneginf(L).all()
+
+
+# ------------------------------------------------------------------ whole path
+def test_dit_path_tiny_rows_and_properties():
+    w = W.WORKLOADS["tiny"]
+    q, k, v = W.make_qkv(w)
+    pos = W.positions(w)
+    O, L = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
+    rows = np.array([0, 17, 299, 300, 319])
+    Or, Lr = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid, rows=rows)
+    assert np.allclose(Or, O[:, :, rows], atol=1e-14)
+    assert np.array_equal(np.isneginf(Lr), np.isneginf(L[:, :, rows]))
+    assert (O[:, :, 300:] == 0).all() and np.isneginf(L[:, :, 300:]).all()
+    # LSE of N(0,1)-ish scores over 300 keys sits near ln(300) + 1/2
+    assert abs(np.mean(L[:, :, :300]) - (math.log(300) + 0.5)) < 0.3
+
+
+# ------------------------------------------------------------------ negative controls
+def test_negative_control_missing_mask_breaks_pad_invariance():
+    q, k, v = rand_qkv(21, 1, 1, 16, 32, 64)
+    g = W.bf16_bits_to_f32(W.finite_garbage_bits(rng(22), (1, 1, 8, 64))).astype(np.float64)
+    k2 = k.copy(); k2[:, :, 24:] = np.clip(g, -1e3, 1e3)
+    no_mask = lambda q_, k_, v_: oracle.attention(q_, k_, v_, 16, 32)  # plants: pads not dropped
+    assert not np.allclose(no_mask(q, k, v)[0], no_mask(q, k2, v)[0])
+
+
+def test_negative_control_log2_lse_fails_closed_form():
+    _, k, v = rand_qkv(23, 1, 1, 3, 50, 64)
+    q = np.zeros((1, 1, 3, 64))
+    O, L = oracle.attention(q, k, v, 3, 50)
+    planted = L / math.log(2.0)        # plants: LSE reported in base 2
+    assert np.allclose(L, math.log(50))
+    assert not np.allclose(planted, math.log(50))
+
+
+def test_negative_control_missing_permutation_breaks_equivalence():
+    x = rng(24).standard_normal((4, 64))
+    c, s = oracle.rope_tables(rng(25).integers(1, 90, (4, 1)), (64,), 10000.0)
+    assert not np.allclose(oracle.rope_split_halves(x, c, s), oracle.rope_interleaved(x, c, s))
+
+
+def test_negative_control_transposed_operand_fails_bruteforce():
+    q, k, v = rand_qkv(26, 1, 1, 6, 6, 6)
+    O2, _ = oracle.attention_bruteforce(q, k, v, 6, 6)
+    planted, _ = oracle.attention(k, q, v, 6, 6)   # plants: Q and K swapped (S^T)
+    assert not np.allclose(planted, O2, atol=1e-6)
+
+
+def test_negative_control_sign_flip_fails_complex_pin():
+    y = rng(27).standard_normal((5, 16))
+    c, s = oracle.rope_tables(rng(28).integers(1, 40, (5, 1)), (16,), 10000.0)
+    planted = oracle.rope_interleaved(y, c, -s)      # plants: rotation sign flipped
+    z = (y[:, 0::2] + 1j * y[:, 1::2]) * (c + 1j * s)
+    assert not np.allclose(planted[:, 0::2], z.real)
