@@ -1,0 +1,166 @@
+/*
+ * dit_attn.h -- C ABI of the MI355X (gfx950) DiT self-attention library.
+ *
+ * One GPU's part of full-sequence self-attention inside a video/image
+ * diffusion transformer after a Ulysses head split: all S tokens, a share of
+ * the heads. The calls follow the pages' problem statement:
+ *   - split-halves RoPE tables and rotation (Difflet PR #153 "TPU sequence
+ *     parallelism ...": FLUX split-RoPE commit and the Wan padding + split
+ *     RoPE commit);
+ *   - attention forward returning O and the natural-log log-sum-exp per query
+ *     row, with tail-pad keys dropped exactly (mstar PR #376, ragged attention
+ *     "return_lse"; maxdiffusion PR #491, the ragged KV tail carries the real
+ *     length);
+ *   - the merge of per-key-shard (O, LSE) pairs (mstar PR #376,
+ *     attention_over_sharded_keys);
+ *   - tail pad / unpad of token rows (Difflet PR #153 Wan padding commit;
+ *     maxdiffusion PR #491 lane padding).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers unless stated otherwise. The
+ *     caller owns every buffer; the library never allocates or frees device
+ *     memory and keeps no state between calls.
+ *   - bf16 data is passed as 16-bit storage (uint16_t bit patterns).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on `stream` and returns without
+ *     synchronising. Outputs must not alias inputs.
+ *   - Arguments are validated before any HIP call. A bad argument returns
+ *     DIT_ERR_INVALID; a valid request the kernels do not cover returns
+ *     DIT_ERR_UNSUPPORTED (there is no silent fallback); a failed launch
+ *     returns DIT_ERR_HIP. dit_last_error() then describes the failure.
+ *     Nothing throws across the ABI.
+ */
+#ifndef DIT_ATTN_H_
+#define DIT_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define DIT_API __attribute__((visibility("default")))
+#else
+#define DIT_API
+#endif
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_ERR_INVALID = -1,
+  DIT_ERR_UNSUPPORTED = -2,
+  DIT_ERR_HIP = -3
+} dit_status;
+
+typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
+
+/*
+ * Attention forward descriptor.
+ *
+ * Q, K, V, O are logically [B, H, S, d] with d contiguous. Element strides
+ * for (b, h, s) are given per tensor; a stride triple of all zeros means the
+ * dense [B, H, S, d] layout. (A [B, S, H, d] caller passes
+ * strides {S*H*d, d, H*d}.) Strides must be multiples of 8 elements and the
+ * base pointers 16-byte aligned (else DIT_ERR_UNSUPPORTED).
+ *
+ * Rows s >= q_valid of Q and s >= kv_valid of K/V are tail pads: pad keys take
+ * no part in any softmax (their content, even NaN or Inf, cannot change a
+ * result), and pad query rows get O = +0.0 and LSE = -inf. With kv_valid == 0
+ * every row gets O = 0 and LSE = -inf (-inf is the identity of the merge).
+ *
+ * RoPE (split halves: channel i pairs with i + d/2, i < d/2):
+ *   x'_i = x_i c_i - x_{i+d/2} s_i,  x'_{i+d/2} = x_{i+d/2} c_i + x_i s_i
+ * computed in fp32 from the bf16 inputs and fp32 tables, rounded once to
+ * bf16 (round to nearest even). cos_q/sin_q are fp32 [s_q, d/2] tables for
+ * the query rows, cos_k/sin_k fp32 [s_kv, d/2] for the key rows (for a key
+ * shard, pass the table pointers offset to the shard's first row). Each pair
+ * must be both NULL (no rotation) or both non-NULL.
+ *
+ * Scores are sm_scale * <q'_i, k'_j> (sm_scale == 0 selects 1/sqrt(d); it
+ * must be finite and positive). Both contractions run on bf16 MFMA with fp32
+ * accumulation; softmax probabilities are rounded to bf16 before P.V.
+ *
+ * Outputs: O in o_dtype (DIT_BF16 for a final result, DIT_F32 for a partial
+ * result that dit_lse_merge will combine), written for rows [0, s_q).
+ * lse: fp32 dense [B, H, s_q], natural log, or NULL to skip it.
+ *
+ * workspace: device scratch for the once-per-call K rotation; required
+ * (non-NULL, 256-byte aligned, at least dit_attn_workspace_size() bytes) when
+ * cos_k/sin_k are given, ignored otherwise. The caller owns it.
+ */
+typedef struct dit_attn_desc {
+  int32_t B, H, d;               /* d in {64, 128}, else DIT_ERR_UNSUPPORTED */
+  int32_t s_q, s_kv;             /* rows present in Q/O and in K/V (padded lengths) */
+  int32_t q_valid, kv_valid;     /* real tokens, 0 <= valid <= s */
+  int32_t o_dtype;               /* dit_dtype */
+  const void *q, *k, *v;         /* bf16 */
+  void *o;                       /* bf16 or fp32 per o_dtype */
+  float *lse;                    /* fp32 [B, H, s_q] or NULL */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];  /* (b, h, s) in elements */
+  float sm_scale;
+  const float *cos_q, *sin_q;    /* fp32 [s_q, d/2] or NULL */
+  const float *cos_k, *sin_k;    /* fp32 [s_kv, d/2] or NULL */
+  void *workspace;
+  size_t workspace_bytes;
+} dit_attn_desc;
+
+/* Bytes of workspace dit_attn_fwd needs for `desc` (0 when K is not rotated). */
+DIT_API int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes);
+
+/* Attention forward with fused RoPE and exact pad-key masking; see above. */
+DIT_API int dit_attn_fwd(const dit_attn_desc *desc, void *stream);
+
+/*
+ * Merge n_parts partial results over disjoint key shards of the same queries
+ * (mstar PR #376, attention_over_sharded_keys). For every row (b, h, i):
+ *   M = max_k L_k;  w_k = exp(L_k - M);  L = M + ln(sum_k w_k);
+ *   O = sum_k w_k O_k / sum_k w_k.
+ * A row whose parts are all -inf gives O = 0, L = -inf; rows i >= q_valid
+ * give O = 0, L = -inf. o_parts / lse_parts are HOST arrays of n_parts device
+ * pointers to dense [B, H, S, d] (part_dtype) and [B, H, S] fp32 tensors.
+ * o_out is dense [B, H, S, d] in out_dtype; lse_out fp32 [B, H, S] or NULL.
+ * 1 <= n_parts <= 16; d in {64, 128}.
+ */
+DIT_API int dit_lse_merge(int n_parts, const void *const *o_parts, const float *const *lse_parts,
+                  int part_dtype, int B, int H, int S, int d, int q_valid,
+                  void *o_out, int out_dtype, float *lse_out, void *stream);
+
+/*
+ * Split-halves RoPE tables from integer positions (Difflet PR #153, FLUX
+ * split-RoPE commit: tables built once per forward). pos: device int32
+ * [S, n_axes]. axis_channels: HOST array of n_axes even channel counts
+ * summing to d (t, h, w order). Axis a owns d/2 pair columns
+ * [P_a, P_a + c_a/2) with P_a = sum_{b<a} c_b/2, and pair j of axis a turns at
+ * theta^(-2j/c_a) per position step:
+ *   cos_out[s, P_a + j] = cos(pos[s, a] * theta^(-2j/c_a)), sin_out likewise.
+ * Angles and sines are evaluated in fp64 and rounded to fp32. Position 0 is
+ * the identity rotation (text tokens, pad rows). cos_out/sin_out: device fp32
+ * [S, d/2]. 1 <= n_axes <= 8, 2 <= d <= 256.
+ */
+DIT_API int dit_rope_split_tables(const int32_t *pos, int S, int n_axes, const int32_t *axis_channels,
+                          int d, float theta, float *cos_out, float *sin_out, void *stream);
+
+/*
+ * Tail padding of token rows: in [B, s_valid, row_bytes] -> out
+ * [B, s_pad, row_bytes], rows >= s_valid of `out` set to zero bytes
+ * (Difflet PR #153 Wan padding commit, 4680 -> 4736).
+ */
+DIT_API int dit_pad_tokens(const void *in, void *out, int B, int s_valid, int s_pad,
+                   int64_t row_bytes, void *stream);
+
+/* Inverse of dit_pad_tokens: in [B, s_pad, row_bytes] -> out [B, s_valid, row_bytes]. */
+DIT_API int dit_unpad_tokens(const void *in, void *out, int B, int s_pad, int s_valid,
+                     int64_t row_bytes, void *stream);
+
+/* Host helper: *s_pad_out = ceil(s_valid / multiple) * multiple. */
+DIT_API int dit_plan_padding(int s_valid, int multiple, int *s_pad_out);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+DIT_API const char *dit_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H_ */

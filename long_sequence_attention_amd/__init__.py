@@ -1,0 +1,210 @@
+"""Python binding of the MI355X DiT self-attention library (libditattn.so).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI (include/dit_attn.h). torch supplies device memory and the
+current stream. Function names follow the C entry points without the `dit_`
+prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _native as N
+from ._native import DitError  # noqa: F401
+
+__all__ = ["attn_fwd", "lse_merge", "rope_split_tables", "pad_tokens", "unpad_tokens",
+           "plan_padding", "library_path", "attn_workspace_size"]
+
+
+def library_path() -> str:
+    N.lib()
+    return N.LIB_PATH
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _strides4(name, t):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, S, d] (any layout with d contiguous)")
+    if t.stride(-1) != 1:
+        raise NotImplementedError(f"{name}: the head dimension must be contiguous")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def plan_padding(s_valid: int, multiple: int) -> int:
+    out = ctypes.c_int()
+    N.check(N.lib().dit_plan_padding(int(s_valid), int(multiple), ctypes.byref(out)), "plan_padding")
+    return out.value
+
+
+def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale):
+    B, H, s_q, d = q.shape
+    desc = N.AttnDesc()
+    desc.B, desc.H, desc.d = B, H, d
+    desc.s_q, desc.s_kv = s_q, k.shape[2]
+    desc.q_valid, desc.kv_valid = q_valid, kv_valid
+    desc.o_dtype = N.DIT_F32 if o.dtype == torch.float32 else N.DIT_BF16
+    desc.q, desc.k, desc.v, desc.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    desc.lse = lse.data_ptr() if lse is not None else None
+    for field, t, name in (("q_stride", q, "q"), ("k_stride", k, "k"), ("v_stride", v, "v"), ("o_stride", o, "out")):
+        getattr(desc, field)[:] = _strides4(name, t)
+    desc.sm_scale = float(sm_scale)
+    if rope_q is not None:
+        desc.cos_q, desc.sin_q = rope_q[0].data_ptr(), rope_q[1].data_ptr()
+    if rope_k is not None:
+        desc.cos_k, desc.sin_k = rope_k[0].data_ptr(), rope_k[1].data_ptr()
+    return desc
+
+
+def attn_workspace_size(q, k, v, *, kv_valid=None, rope_k=None) -> int:
+    """Workspace bytes attn_fwd needs (the once-per-call rotated K)."""
+    kv_valid = k.shape[2] if kv_valid is None else int(kv_valid)
+    if rope_k is None or kv_valid == 0:
+        return 0
+    B, H, s_kv, d = k.shape
+    return (B * H * s_kv * d * 2 + 255) // 256 * 256
+
+
+def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
+             out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None):
+    """Attention forward (dit_attn_fwd).
+
+    q: [B, H, s_q, d], k/v: [B, H, s_kv, d] bf16 device tensors, any strides
+    with d contiguous (e.g. a permuted [B, S, H, d] buffer). Rows >= q_valid /
+    kv_valid are tail pads. rope_q / rope_k: (cos, sin) fp32 [S, d/2] tables
+    or None. Returns (O, LSE) with O [B, H, s_q, d] in out_dtype (or `out`)
+    and LSE fp32 [B, H, s_q] (natural log), or O alone if return_lse=False.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(name, t, torch.bfloat16)
+    B, H, s_q, d = q.shape
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    q_valid = s_q if q_valid is None else int(q_valid)
+    kv_valid = k.shape[2] if kv_valid is None else int(kv_valid)
+    for name, tab, rows in (("rope_q", rope_q, s_q), ("rope_k", rope_k, k.shape[2])):
+        if tab is not None:
+            for t in tab:
+                _need_cuda(name, t, torch.float32)
+                if t.shape != (rows, d // 2) or not t.is_contiguous():
+                    raise ValueError(f"{name} tables must be contiguous fp32 [{rows}, {d // 2}]")
+    if out is None:
+        out = torch.empty((B, H, s_q, d), dtype=out_dtype, device=q.device)
+    else:
+        _need_cuda("out", out)
+        if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != (B, H, s_q, d):
+            raise ValueError("out must be bf16 or fp32 [B, H, s_q, d]")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, s_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if lse.shape != (B, H, s_q) or not lse.is_contiguous():
+            raise ValueError("lse must be contiguous fp32 [B, H, s_q]")
+    desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale)
+    need = ctypes.c_size_t()
+    N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")
+    if need.value:
+        if workspace is None:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        if workspace.numel() * workspace.element_size() < need.value:
+            raise ValueError(f"workspace needs {need.value} bytes")
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    N.check(N.lib().dit_attn_fwd(ctypes.byref(desc), _stream(q.device)), "attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def lse_merge(o_parts, lse_parts, *, q_valid=None, out_dtype=torch.bfloat16, out=None, lse_out=None,
+              return_lse=True):
+    """Merge partial (O, LSE) results over key shards (dit_lse_merge).
+
+    o_parts: list of dense [B, H, S, d] bf16/fp32 tensors (one dtype);
+    lse_parts: list of dense fp32 [B, H, S].
+    """
+    n = len(o_parts)
+    if n != len(lse_parts) or n == 0:
+        raise ValueError("need matching, non-empty lists of O and LSE parts")
+    B, H, S, d = o_parts[0].shape
+    pdt = o_parts[0].dtype
+    for o, l in zip(o_parts, lse_parts):
+        _need_cuda("o_part", o)
+        _need_cuda("lse_part", l, torch.float32)
+        if o.dtype != pdt or o.shape != (B, H, S, d) or not o.is_contiguous():
+            raise ValueError("O parts must share dtype and be dense [B, H, S, d]")
+        if l.shape != (B, H, S) or not l.is_contiguous():
+            raise ValueError("LSE parts must be dense fp32 [B, H, S]")
+    q_valid = S if q_valid is None else int(q_valid)
+    dev = o_parts[0].device
+    if out is None:
+        out = torch.empty((B, H, S, d), dtype=out_dtype, device=dev)
+    if lse_out is None and return_lse:
+        lse_out = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    optr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in o_parts])
+    lptr = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
+    rc = N.lib().dit_lse_merge(n, optr, lptr, N.DIT_F32 if pdt == torch.float32 else N.DIT_BF16,
+                               B, H, S, d, q_valid, _ptr(out),
+                               N.DIT_F32 if out.dtype == torch.float32 else N.DIT_BF16,
+                               _ptr(lse_out), _stream(dev))
+    N.check(rc, "lse_merge")
+    return (out, lse_out) if return_lse else out
+
+
+def rope_split_tables(pos, axis_channels, d: int, theta: float = 10000.0):
+    """cos, sin fp32 [S, d/2] from int32 positions [S, n_axes] (dit_rope_split_tables)."""
+    _need_cuda("pos", pos, torch.int32)
+    if pos.dim() == 1:
+        pos = pos[:, None]
+    pos = pos.contiguous()
+    S, n_axes = pos.shape
+    chans = (ctypes.c_int32 * len(axis_channels))(*[int(c) for c in axis_channels])
+    if len(axis_channels) != n_axes:
+        raise ValueError("one channel count per position column")
+    cos = torch.empty((S, d // 2), dtype=torch.float32, device=pos.device)
+    sin = torch.empty_like(cos)
+    N.check(N.lib().dit_rope_split_tables(_ptr(pos), S, n_axes, chans, int(d), float(theta), _ptr(cos),
+                                          _ptr(sin), _stream(pos.device)), "rope_split_tables")
+    return cos, sin
+
+
+def pad_tokens(x, s_pad: int, out=None):
+    """[B, s_valid, ...] -> [B, s_pad, ...] with zero tail rows (dit_pad_tokens)."""
+    _need_cuda("x", x)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    B, s_valid = x.shape[:2]
+    row_bytes = x.element_size() * math.prod(x.shape[2:])
+    if out is None:
+        out = torch.empty((B, s_pad) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
+    N.check(N.lib().dit_pad_tokens(_ptr(x), _ptr(out), B, s_valid, int(s_pad), row_bytes, _stream(x.device)),
+            "pad_tokens")
+    return out
+
+
+def unpad_tokens(x, s_valid: int, out=None):
+    """[B, s_pad, ...] -> [B, s_valid, ...] (dit_unpad_tokens)."""
+    _need_cuda("x", x)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    B, s_pad = x.shape[:2]
+    row_bytes = x.element_size() * math.prod(x.shape[2:])
+    if out is None:
+        out = torch.empty((B, int(s_valid)) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
+    N.check(N.lib().dit_unpad_tokens(_ptr(x), _ptr(out), B, s_pad, int(s_valid), row_bytes, _stream(x.device)),
+            "unpad_tokens")
+    return out

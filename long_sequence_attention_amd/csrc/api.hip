@@ -1,0 +1,277 @@
+// C ABI of the library: argument validation (before any HIP call), launch
+// geometry and status codes. Declarations and contracts: include/dit_attn.h.
+#include "dit_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[1024];
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DIT_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(DIT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Resolve a (b, h, s) stride triple; all zeros means dense [B, H, S, d].
+void resolve_strides(const int64_t in[3], int H, int S, int d, int64_t out[3]) {
+  if (in[0] == 0 && in[1] == 0 && in[2] == 0) {
+    out[0] = (int64_t)H * S * d;
+    out[1] = (int64_t)S * d;
+    out[2] = d;
+  } else {
+    out[0] = in[0];
+    out[1] = in[1];
+    out[2] = in[2];
+  }
+}
+
+int check_strides(const char *name, const int64_t st[3]) {
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return fail(DIT_ERR_UNSUPPORTED, "%s stride[%d] = %lld: negative strides are not supported", name, i, (long long)st[i]);
+    if (st[i] % 8 != 0)
+      return fail(DIT_ERR_UNSUPPORTED, "%s stride[%d] = %lld: strides must be multiples of 8 elements", name, i, (long long)st[i]);
+  }
+  return DIT_OK;
+}
+
+size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+int validate_attn(const dit_attn_desc *d, float *scale_out) {
+  if (d == nullptr) return fail(DIT_ERR_INVALID, "desc is NULL");
+  if (d->B < 1 || d->H < 1) return fail(DIT_ERR_INVALID, "B and H must be >= 1 (B=%d, H=%d)", d->B, d->H);
+  if (d->d <= 0 || (d->d % 2) != 0) return fail(DIT_ERR_INVALID, "head dim d=%d must be positive and even", d->d);
+  if (d->d != 64 && d->d != 128) return fail(DIT_ERR_UNSUPPORTED, "head dim d=%d: kernels exist for d in {64, 128}", d->d);
+  if (d->s_q < 0 || d->s_kv < 0) return fail(DIT_ERR_INVALID, "s_q and s_kv must be >= 0");
+  if (d->q_valid < 0 || d->q_valid > d->s_q)
+    return fail(DIT_ERR_INVALID, "q_valid=%d must lie in [0, s_q=%d]", d->q_valid, d->s_q);
+  if (d->kv_valid < 0 || d->kv_valid > d->s_kv)
+    return fail(DIT_ERR_INVALID, "kv_valid=%d must lie in [0, s_kv=%d]", d->kv_valid, d->s_kv);
+  if (d->o_dtype != DIT_BF16 && d->o_dtype != DIT_F32) return fail(DIT_ERR_INVALID, "o_dtype=%d is not a dit_dtype", d->o_dtype);
+  if (d->s_q > 0 && (d->q == nullptr || d->o == nullptr)) return fail(DIT_ERR_INVALID, "q and o must be non-NULL when s_q > 0");
+  if (d->kv_valid > 0 && (d->k == nullptr || d->v == nullptr))
+    return fail(DIT_ERR_INVALID, "k and v must be non-NULL when kv_valid > 0");
+  if ((d->cos_q == nullptr) != (d->sin_q == nullptr)) return fail(DIT_ERR_INVALID, "cos_q and sin_q must both be given or both be NULL");
+  if ((d->cos_k == nullptr) != (d->sin_k == nullptr)) return fail(DIT_ERR_INVALID, "cos_k and sin_k must both be given or both be NULL");
+  float scale = d->sm_scale;
+  if (scale == 0.0f) scale = 1.0f / std::sqrt((float)d->d);
+  if (!std::isfinite(scale) || scale < 0.0f) return fail(DIT_ERR_INVALID, "sm_scale=%g must be finite and positive", (double)d->sm_scale);
+  const int64_t nq = ((int64_t)d->s_q + 127) / 128;
+  if (nq * d->H * d->B > 0x7fffffffLL) return fail(DIT_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  const void *ptrs[] = {d->q, d->k, d->v, d->o, d->cos_q, d->sin_q, d->cos_k, d->sin_k};
+  for (const void *p : ptrs)
+    if (p != nullptr && !aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+  if (d->lse != nullptr && (reinterpret_cast<uintptr_t>(d->lse) & 3u)) return fail(DIT_ERR_INVALID, "lse must be 4-byte aligned");
+  int64_t st[3];
+  int rc;
+  resolve_strides(d->q_stride, d->H, d->s_q, d->d, st);
+  if ((rc = check_strides("q", st)) != DIT_OK) return rc;
+  resolve_strides(d->k_stride, d->H, d->s_kv, d->d, st);
+  if ((rc = check_strides("k", st)) != DIT_OK) return rc;
+  resolve_strides(d->v_stride, d->H, d->s_kv, d->d, st);
+  if ((rc = check_strides("v", st)) != DIT_OK) return rc;
+  resolve_strides(d->o_stride, d->H, d->s_q, d->d, st);
+  if ((rc = check_strides("o", st)) != DIT_OK) return rc;
+  *scale_out = scale;
+  return DIT_OK;
+}
+
+size_t attn_workspace_bytes(const dit_attn_desc *d) {
+  if (d->cos_k == nullptr || d->kv_valid == 0) return 0;
+  return round_up((size_t)d->B * d->H * (size_t)d->s_kv * d->d * 2, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dit_last_error(void) { return g_err; }
+
+int dit_plan_padding(int s_valid, int multiple, int *s_pad_out) {
+  if (s_pad_out == nullptr) return fail(DIT_ERR_INVALID, "s_pad_out is NULL");
+  if (multiple <= 0 || s_valid < 0) return fail(DIT_ERR_INVALID, "need multiple > 0 and s_valid >= 0");
+  const int64_t r = ((int64_t)s_valid + multiple - 1) / multiple * multiple;
+  if (r > 0x7fffffffLL) return fail(DIT_ERR_INVALID, "padded length overflows int");
+  *s_pad_out = (int)r;
+  return ok();
+}
+
+int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes) {
+  if (bytes == nullptr) return fail(DIT_ERR_INVALID, "bytes is NULL");
+  float scale;
+  const int rc = validate_attn(desc, &scale);
+  if (rc != DIT_OK) return rc;
+  *bytes = attn_workspace_bytes(desc);
+  return ok();
+}
+
+int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
+  float scale;
+  int rc = validate_attn(desc, &scale);
+  if (rc != DIT_OK) return rc;
+  const dit_attn_desc &d = *desc;
+  const size_t need = attn_workspace_bytes(desc);
+  if (need > 0) {
+    if (d.workspace == nullptr || d.workspace_bytes < need)
+      return fail(DIT_ERR_INVALID, "workspace of %zu bytes required for the K rotation (got %zu)", need,
+                  d.workspace == nullptr ? (size_t)0 : d.workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(d.workspace) & 255u) != 0) return fail(DIT_ERR_INVALID, "workspace must be 256-byte aligned");
+  }
+  if (d.s_q == 0) return ok();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  dit::AttnParams p{};
+  int64_t s3[3];
+  resolve_strides(d.q_stride, d.H, d.s_q, d.d, s3);
+  p.qs_b = s3[0]; p.qs_h = s3[1]; p.qs_s = s3[2];
+  resolve_strides(d.k_stride, d.H, d.s_kv, d.d, s3);
+  p.ks_b = s3[0]; p.ks_h = s3[1]; p.ks_s = s3[2];
+  resolve_strides(d.v_stride, d.H, d.s_kv, d.d, s3);
+  p.vs_b = s3[0]; p.vs_h = s3[1]; p.vs_s = s3[2];
+  resolve_strides(d.o_stride, d.H, d.s_q, d.d, s3);
+  p.os_b = s3[0]; p.os_h = s3[1]; p.os_s = s3[2];
+  p.q = static_cast<const dit::bf16_t *>(d.q);
+  p.k = static_cast<const dit::bf16_t *>(d.k);
+  p.v = static_cast<const dit::bf16_t *>(d.v);
+  p.o = d.o;
+  p.lse = d.lse;
+  p.cos_q = d.cos_q;
+  p.sin_q = d.sin_q;
+  p.B = d.B; p.H = d.H; p.s_q = d.s_q; p.s_kv = d.s_kv;
+  p.q_valid = d.q_valid; p.kv_valid = d.kv_valid;
+  p.o_f32 = d.o_dtype == DIT_F32;
+  p.n_qtiles = (d.s_q + 127) / 128;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  if (need > 0) {
+    dit::RopeRotateParams r{};
+    r.x = p.k;
+    r.y = static_cast<dit::bf16_t *>(d.workspace);
+    r.cos_t = d.cos_k;
+    r.sin_t = d.sin_k;
+    r.xs_b = p.ks_b; r.xs_h = p.ks_h; r.xs_s = p.ks_s;
+    r.B = d.B; r.H = d.H; r.S = d.s_kv; r.valid = d.kv_valid; r.d = d.d;
+    rc = hip_status(dit::launch_rope_rotate(r, st), "K rotation launch");
+    if (rc != DIT_OK) return rc;
+    p.k = r.y;
+    p.ks_b = (int64_t)d.H * d.s_kv * d.d;
+    p.ks_h = (int64_t)d.s_kv * d.d;
+    p.ks_s = d.d;
+  }
+  return hip_status(dit::launch_attn_fwd(p, d.d, st), "attention launch");
+}
+
+int dit_lse_merge(int n_parts, const void *const *o_parts, const float *const *lse_parts, int part_dtype, int B,
+                  int H, int S, int d, int q_valid, void *o_out, int out_dtype, float *lse_out, void *stream) {
+  if (n_parts < 1 || n_parts > dit::kMaxMergeParts)
+    return fail(DIT_ERR_INVALID, "n_parts=%d must lie in [1, %d]", n_parts, dit::kMaxMergeParts);
+  if (o_parts == nullptr || lse_parts == nullptr) return fail(DIT_ERR_INVALID, "o_parts and lse_parts must be non-NULL host arrays");
+  if (B < 1 || H < 1 || S < 0) return fail(DIT_ERR_INVALID, "need B >= 1, H >= 1, S >= 0");
+  if (d <= 0 || d % 2) return fail(DIT_ERR_INVALID, "d=%d must be positive and even", d);
+  if (d != 64 && d != 128) return fail(DIT_ERR_UNSUPPORTED, "merge kernels exist for d in {64, 128}");
+  if (q_valid < 0 || q_valid > S) return fail(DIT_ERR_INVALID, "q_valid=%d must lie in [0, S=%d]", q_valid, S);
+  if ((part_dtype != DIT_BF16 && part_dtype != DIT_F32) || (out_dtype != DIT_BF16 && out_dtype != DIT_F32))
+    return fail(DIT_ERR_INVALID, "dtypes must be DIT_BF16 or DIT_F32");
+  if (S > 0 && o_out == nullptr) return fail(DIT_ERR_INVALID, "o_out is NULL");
+  for (int k = 0; k < n_parts; ++k) {
+    if (S > 0 && (o_parts[k] == nullptr || lse_parts[k] == nullptr))
+      return fail(DIT_ERR_INVALID, "part %d has a NULL pointer", k);
+    if ((reinterpret_cast<uintptr_t>(o_parts[k]) & 3u) || (reinterpret_cast<uintptr_t>(lse_parts[k]) & 3u))
+      return fail(DIT_ERR_UNSUPPORTED, "part %d pointers must be 4-byte aligned", k);
+  }
+  if (reinterpret_cast<uintptr_t>(o_out) & 3u) return fail(DIT_ERR_UNSUPPORTED, "o_out must be 4-byte aligned");
+  const int64_t rows = (int64_t)B * H * S;
+  if (rows > 0x7fffffffLL) return fail(DIT_ERR_UNSUPPORTED, "too many rows");
+  if (rows == 0) return ok();
+  dit::MergeParams p{};
+  for (int k = 0; k < n_parts; ++k) {
+    p.o_parts[k] = o_parts[k];
+    p.lse_parts[k] = lse_parts[k];
+  }
+  p.o_out = o_out;
+  p.lse_out = lse_out;
+  p.n_parts = n_parts;
+  p.part_f32 = part_dtype == DIT_F32;
+  p.out_f32 = out_dtype == DIT_F32;
+  p.rows = (int32_t)rows;
+  p.S = S;
+  p.d = d;
+  p.q_valid = q_valid;
+  return hip_status(dit::launch_lse_merge(p, reinterpret_cast<hipStream_t>(stream)), "merge launch");
+}
+
+int dit_rope_split_tables(const int32_t *pos, int S, int n_axes, const int32_t *axis_channels, int d, float theta,
+                          float *cos_out, float *sin_out, void *stream) {
+  if (S < 0) return fail(DIT_ERR_INVALID, "S must be >= 0");
+  if (n_axes < 1 || n_axes > 8) return fail(DIT_ERR_INVALID, "n_axes=%d must lie in [1, 8]", n_axes);
+  if (axis_channels == nullptr) return fail(DIT_ERR_INVALID, "axis_channels is NULL");
+  if (d < 2 || d > 2 * dit::kMaxPairs || d % 2) return fail(DIT_ERR_INVALID, "d=%d must be even and in [2, %d]", d, 2 * dit::kMaxPairs);
+  if (!(theta > 0.0f) || !std::isfinite(theta)) return fail(DIT_ERR_INVALID, "theta must be finite and positive");
+  int sum = 0;
+  for (int a = 0; a < n_axes; ++a) {
+    if (axis_channels[a] <= 0 || axis_channels[a] % 2)
+      return fail(DIT_ERR_INVALID, "axis %d has %d channels: each axis needs a positive even count", a, axis_channels[a]);
+    sum += axis_channels[a];
+  }
+  if (sum != d) return fail(DIT_ERR_INVALID, "axis channels sum to %d, not d=%d", sum, d);
+  if (S > 0 && (pos == nullptr || cos_out == nullptr || sin_out == nullptr))
+    return fail(DIT_ERR_INVALID, "pos, cos_out and sin_out must be non-NULL");
+  if (S == 0) return ok();
+  dit::TableParams p{};
+  int j = 0;
+  for (int a = 0; a < n_axes; ++a) {
+    const int c = axis_channels[a];
+    for (int k = 0; k < c / 2; ++k, ++j) {
+      p.freq[j] = std::pow((double)theta, -2.0 * k / (double)c);
+      p.axis[j] = (uint8_t)a;
+    }
+  }
+  p.pos = pos;
+  p.cos_out = cos_out;
+  p.sin_out = sin_out;
+  p.S = S;
+  p.n_axes = n_axes;
+  p.half_d = d / 2;
+  return hip_status(dit::launch_rope_tables(p, reinterpret_cast<hipStream_t>(stream)), "table launch");
+}
+
+int dit_pad_tokens(const void *in, void *out, int B, int s_valid, int s_pad, int64_t row_bytes, void *stream) {
+  if (B < 1 || s_valid < 0 || s_pad < s_valid || row_bytes <= 0)
+    return fail(DIT_ERR_INVALID, "need B >= 1, 0 <= s_valid <= s_pad, row_bytes > 0");
+  if (s_pad > 0 && out == nullptr) return fail(DIT_ERR_INVALID, "out is NULL");
+  if (s_valid > 0 && in == nullptr) return fail(DIT_ERR_INVALID, "in is NULL");
+  if (in != nullptr && in == out) return fail(DIT_ERR_INVALID, "in and out must not alias");
+  return hip_status(dit::launch_row_copy(in, out, B, s_valid, s_pad, s_valid, row_bytes, reinterpret_cast<hipStream_t>(stream)),
+                    "pad launch");
+}
+
+int dit_unpad_tokens(const void *in, void *out, int B, int s_pad, int s_valid, int64_t row_bytes, void *stream) {
+  if (B < 1 || s_valid < 0 || s_pad < s_valid || row_bytes <= 0)
+    return fail(DIT_ERR_INVALID, "need B >= 1, 0 <= s_valid <= s_pad, row_bytes > 0");
+  if (s_valid > 0 && (out == nullptr || in == nullptr)) return fail(DIT_ERR_INVALID, "in and out must be non-NULL");
+  if (in != nullptr && in == out) return fail(DIT_ERR_INVALID, "in and out must not alias (no in-place unpad)");
+  return hip_status(dit::launch_row_copy(in, out, B, s_pad, s_valid, s_valid, row_bytes, reinterpret_cast<hipStream_t>(stream)),
+                    "unpad launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Shared device helpers and launcher declarations for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef uint16_t bf16_t;  // bf16 storage
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 -> fp32 is exact: the pattern is the top half of the fp32 pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// Parameters of the attention forward kernel (passed by value).
+struct AttnParams {
+  const bf16_t *q, *k, *v;
+  void *o;
+  float *lse;
+  int64_t qs_b, qs_h, qs_s;
+  int64_t ks_b, ks_h, ks_s;
+  int64_t vs_b, vs_h, vs_s;
+  int64_t os_b, os_h, os_s;
+  const float *cos_q, *sin_q;
+  int32_t B, H, s_q, s_kv, q_valid, kv_valid;
+  int32_t o_f32;
+  int32_t n_qtiles;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+// Parameters of the K rotation pre-pass.
+struct RopeRotateParams {
+  const bf16_t *x;
+  bf16_t *y;  // dense [B, H, S, d]
+  const float *cos_t, *sin_t;
+  int64_t xs_b, xs_h, xs_s;
+  int32_t B, H, S, valid, d;
+};
+
+constexpr int kMaxMergeParts = 16;
+struct MergeParams {
+  const void *o_parts[kMaxMergeParts];
+  const float *lse_parts[kMaxMergeParts];
+  void *o_out;
+  float *lse_out;
+  int32_t n_parts, part_f32, out_f32, rows, S, d, q_valid;
+};
+
+constexpr int kMaxPairs = 128;
+struct TableParams {
+  double freq[kMaxPairs];
+  uint8_t axis[kMaxPairs];
+  const int32_t *pos;
+  float *cos_out, *sin_out;
+  int32_t S, n_axes, half_d;
+};
+
+// Launchers (host side, defined next to their kernels). Return hipError_t.
+hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream);
+hipError_t launch_rope_rotate(const RopeRotateParams &p, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
+hipError_t launch_rope_tables(const TableParams &p, hipStream_t stream);
+hipError_t launch_row_copy(const void *in, void *out, int B, int s_in, int s_out, int n_copy,
+                           int64_t row_bytes, hipStream_t stream);
+
+}  // namespace dit

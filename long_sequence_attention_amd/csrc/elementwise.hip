@@ -1,0 +1,147 @@
+// HBM-bound passes of the DiT attention path on gfx950:
+//   * RoPE cos/sin tables from integer positions (Difflet PR #153, FLUX
+//     split-RoPE commit: tables built once per forward, split-halves order);
+//   * tail pad / unpad of token rows (Difflet PR #153 Wan padding commit;
+//     maxdiffusion PR #491 lane padding);
+//   * the LSE merge of per-key-shard partial results (mstar PR #376,
+//     attention_over_sharded_keys).
+// Each is a streaming pass: 16-byte vector loads/stores, consecutive lanes on
+// consecutive addresses, no LDS.
+#include "common.h"
+
+namespace dit {
+
+namespace {
+
+// One thread per table entry (s, pair j): angle = pos[s, axis(j)] * freq[j]
+// evaluated in fp64, cos/sin in fp64, rounded once to fp32.
+__global__ __launch_bounds__(256) void rope_tables_kernel(TableParams p) {
+  const int64_t total = (int64_t)p.S * p.half_d;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int s = (int)(t / p.half_d);
+    const int j = (int)(t % p.half_d);
+    const double ang = (double)p.pos[(int64_t)s * p.n_axes + p.axis[j]] * p.freq[j];
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    p.cos_out[t] = (float)cs;
+    p.sin_out[t] = (float)sn;
+  }
+}
+
+// out row s of batch b = in row s for s < n_copy, else zero. V is the copy
+// granule (16, 4 or 1 bytes), chosen from the row size and alignment.
+template <typename V>
+__global__ __launch_bounds__(256) void row_copy_kernel(const V *__restrict__ in, V *__restrict__ out,
+                                                      int s_in, int s_out, int n_copy,
+                                                      int64_t row_vec, int64_t total) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / row_vec;
+    const int64_t v = t - r * row_vec;
+    const int64_t b = r / s_out;
+    const int64_t s = r - b * s_out;
+    V val{};
+    if (s < n_copy) val = in[(b * s_in + s) * row_vec + v];
+    out[t] = val;
+  }
+}
+
+// 32 lanes per (b, h, i) row; each lane owns d/32 consecutive channels.
+template <int PER>
+__global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= p.rows) return;
+  const int sub = threadIdx.x & 31;
+  const int i = (int)(row % p.S);
+  float L[kMaxMergeParts];
+  float M = -INFINITY;
+  for (int k = 0; k < p.n_parts; ++k) {
+    L[k] = p.lse_parts[k][row];
+    M = fmaxf(M, L[k]);
+  }
+  const bool empty = (M == -INFINITY) || (i >= p.q_valid);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (!empty) {
+    for (int k = 0; k < p.n_parts; ++k) {
+      const float w = expf(L[k] - M);
+      wsum += w;
+      const int64_t off = row * p.d + sub * PER;
+      if (p.part_f32) {
+        const float *src = reinterpret_cast<const float *>(p.o_parts[k]) + off;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+      } else {
+        const bf16_t *src = reinterpret_cast<const bf16_t *>(p.o_parts[k]) + off;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, __uint_as_float((uint32_t)src[e] << 16), acc[e]);
+      }
+    }
+  }
+  const float inv = empty ? 0.f : 1.0f / wsum;
+  const int64_t off = row * p.d + sub * PER;
+  if (p.out_f32) {
+    float *dst = reinterpret_cast<float *>(p.o_out) + off;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[e] = empty ? 0.f : acc[e] * inv;
+  } else {
+    bf16_t *dst = reinterpret_cast<bf16_t *>(p.o_out) + off;
+#pragma unroll
+    for (int e = 0; e < PER; e += 2) {
+      const uint32_t w = pack_bf16x2(empty ? 0.f : acc[e] * inv, empty ? 0.f : acc[e + 1] * inv);
+      *reinterpret_cast<uint32_t *>(dst + e) = w;
+    }
+  }
+  if (p.lse_out != nullptr && sub == 0) p.lse_out[row] = empty ? -INFINITY : M + logf(wsum);
+}
+
+int grid_for(int64_t total) {
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  return (int)(blocks < 1 ? 1 : blocks);
+}
+
+}  // namespace
+
+hipError_t launch_rope_tables(const TableParams &p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.S * p.half_d;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_tables_kernel, dim3(grid_for(total)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_copy(const void *in, void *out, int B, int s_in, int s_out, int n_copy,
+                           int64_t row_bytes, hipStream_t stream) {
+  if ((int64_t)B * s_out * row_bytes == 0) return hipSuccess;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out);
+  if (row_bytes % 16 == 0 && a % 16 == 0) {
+    const int64_t rv = row_bytes / 16, total = (int64_t)B * s_out * rv;
+    hipLaunchKernelGGL(row_copy_kernel<uint4>, dim3(grid_for(total)), dim3(256), 0, stream,
+                       (const uint4 *)in, (uint4 *)out, s_in, s_out, n_copy, rv, total);
+  } else if (row_bytes % 4 == 0 && a % 4 == 0) {
+    const int64_t rv = row_bytes / 4, total = (int64_t)B * s_out * rv;
+    hipLaunchKernelGGL(row_copy_kernel<uint32_t>, dim3(grid_for(total)), dim3(256), 0, stream,
+                       (const uint32_t *)in, (uint32_t *)out, s_in, s_out, n_copy, rv, total);
+  } else {
+    const int64_t rv = row_bytes, total = (int64_t)B * s_out * rv;
+    hipLaunchKernelGGL(row_copy_kernel<uint8_t>, dim3(grid_for(total)), dim3(256), 0, stream,
+                       (const uint8_t *)in, (uint8_t *)out, s_in, s_out, n_copy, rv, total);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream) {
+  if (p.rows <= 0) return hipSuccess;
+  const int64_t blocks = ((int64_t)p.rows + 7) / 8;
+  if (p.d == 128) {
+    hipLaunchKernelGGL(lse_merge_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(lse_merge_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dit

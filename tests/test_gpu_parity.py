@@ -1,0 +1,316 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, plus pad invariance, bit-identity and edge cases.
+
+Graded tolerances (bf16 inputs): O max-abs 1.5e-2 and mean-abs 2e-3, LSE
+abs 5e-3. Pad handling is bit-exact: refilling pad rows with other garbage
+(finite, NaN, +-Inf) changes no output bit, and pad query rows are +0.0 with
+LSE -inf.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import (assert_pad_rows, compare, ensure_built, lse_rounding_bound, raw_bits, to_dev_bf16, to_np_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    ensure_built()
+    import long_sequence_attention_amd as ops
+    return ops
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"\n>>> {msg}", flush=True)
+
+
+def gpu_tables(ops, w, pos=None):
+    import torch
+    pos = W.positions(w) if pos is None else pos
+    return ops.rope_split_tables(torch.from_numpy(pos).to(dev()), w.axes, w.d, w.theta)
+
+
+def run_gpu(ops, w, q, k, v, tabs, out_dtype=None, kv_valid=None):
+    import torch
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    o, l = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid if kv_valid is None else kv_valid,
+                        rope_q=tabs, rope_k=tabs, out_dtype=out_dtype or torch.bfloat16)
+    torch.cuda.synchronize()
+    return o, l
+
+
+# ------------------------------------------------------------------ tables
+@pytest.mark.parametrize("name", ["tiny", "flux", "wan480", "hunyuan", "wan720"])
+def test_rope_tables_match_oracle(ops, name):
+    w = W.WORKLOADS[name]
+    say(f"tables {name}")
+    c, s = gpu_tables(ops, w)
+    cr, sr = oracle.rope_tables(W.positions(w), w.axes, w.theta)
+    assert np.abs(to_np_f64(c) - cr).max() < 1e-6
+    assert np.abs(to_np_f64(s) - sr).max() < 1e-6
+    n_grid = int(np.prod(w.grid))
+    assert (to_np_f64(c)[n_grid:] == 1).all() and (to_np_f64(s)[n_grid:] == 0).all()
+
+
+# ------------------------------------------------------------------ full configs
+@pytest.mark.parametrize("name", ["tiny", "flux", "wan480", "hunyuan"])
+def test_parity_full_config(ops, name):
+    w = W.WORKLOADS[name]
+    say(f"parity {name} B={w.B} H={w.H} d={w.d} S={w.s_valid}->{w.s_pad}")
+    q, k, v = W.make_qkv(w)
+    pos = W.positions(w)
+    o, l = run_gpu(ops, w, q, k, v, gpu_tables(ops, w))
+    O_ref, L_ref = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
+    valid = np.arange(w.s_pad) < w.s_valid
+    og, lg = to_np_f64(o), to_np_f64(l)
+    compare(og, lg, O_ref, L_ref, valid, name)
+    assert_pad_rows(og, lg, valid, name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan480", "hunyuan"])
+def test_pad_invariance_bit_exact(ops, name):
+    import torch
+    w = W.WORKLOADS[name]
+    say(f"pad invariance {name}")
+    tabs = gpu_tables(ops, w)
+    q, k, v = W.make_qkv(w)
+    o1, l1 = run_gpu(ops, w, q, k, v, tabs)
+    q2, k2, v2 = W.make_qkv(w, garbage_seed_offset=2000)
+    o2, l2 = run_gpu(ops, w, q2, k2, v2, tabs)
+    assert np.array_equal(raw_bits(o1), raw_bits(o2)) and np.array_equal(raw_bits(l1), raw_bits(l2))
+    # NaN / +Inf / -Inf pad rows
+    for pattern in (0x7FC0, 0x7F80, 0xFF80, 0xFFFF):
+        q3, k3, v3 = (x.copy() for x in (q, k, v))
+        for x in (q3, k3, v3):
+            x[:, :, w.s_valid:] = pattern
+        o3, l3 = run_gpu(ops, w, q3, k3, v3, tabs)
+        assert np.array_equal(raw_bits(o1), raw_bits(o3)), hex(pattern)
+        assert np.array_equal(raw_bits(l1), raw_bits(l3)), hex(pattern)
+    torch.cuda.synchronize()
+
+
+def test_run_to_run_bit_identity_and_nan_canary(ops):
+    import torch
+    w = W.WORKLOADS["wan480"]
+    say("bit identity + canary wan480")
+    tabs = gpu_tables(ops, w)
+    q, k, v = (to_dev_bf16(x) for x in W.make_qkv(w))
+    outs = []
+    for _ in range(3):
+        o = torch.full((w.B, w.H, w.s_pad, w.d), float("nan"), dtype=torch.bfloat16, device=dev())
+        l = torch.full((w.B, w.H, w.s_pad), float("nan"), dtype=torch.float32, device=dev())
+        ops.attn_fwd(q, k, v, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs, out=o, lse=l)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any() and not torch.isnan(l).any()
+        outs.append((raw_bits(o), raw_bits(l)))
+    for a in outs[1:]:
+        assert np.array_equal(a[0], outs[0][0]) and np.array_equal(a[1], outs[0][1])
+
+
+def test_bshd_strided_layout_equals_dense(ops):
+    import torch
+    w = W.WORKLOADS["wan480"]
+    say("BSHD strides wan480")
+    tabs = gpu_tables(ops, w)
+    q, k, v = (to_dev_bf16(x) for x in W.make_qkv(w))
+    o1, l1 = ops.attn_fwd(q, k, v, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs)
+    # the same data held as [B, S, H, d], viewed as [B, H, S, d]
+    qs, ks, vs = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    os_ = torch.empty((w.B, w.s_pad, w.H, w.d), dtype=torch.bfloat16, device=dev()).transpose(1, 2)
+    o2, l2 = ops.attn_fwd(qs, ks, vs, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs, out=os_)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.contiguous().view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ key shards
+def test_wan720_single_pass_and_four_shard_merge(ops):
+    import torch
+    w = W.WORKLOADS["wan720"]
+    say("wan720 single pass + 4 key shards + merge (2048 sampled rows per head)")
+    tabs = gpu_tables(ops, w)
+    cos, sin = tabs
+    q, k, v = W.make_qkv(w)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    o1, l1 = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs)
+    parts_o, parts_l = [], []
+    for (s0, L, kvv) in W.key_shards(w):
+        po, pl = ops.attn_fwd(qd, kd[:, :, s0:s0 + L], vd[:, :, s0:s0 + L], q_valid=w.s_valid, kv_valid=kvv,
+                              rope_q=tabs, rope_k=(cos[s0:s0 + L], sin[s0:s0 + L]), out_dtype=torch.float32)
+        parts_o.append(po)
+        parts_l.append(pl)
+    o2, l2 = ops.lse_merge(parts_o, parts_l, q_valid=w.s_valid)
+    torch.cuda.synchronize()
+    del parts_o, parts_l
+    pos = W.positions(w)
+    for h in range(w.H):
+        rows = np.concatenate([W.sample_rows(w, h), np.arange(w.s_valid, w.s_pad)])
+        O_ref, L_ref = oracle.dit_path(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], pos, pos, w.axes, w.theta,
+                                       w.s_valid, w.s_valid, rows=rows)
+        valid = rows < w.s_valid
+        for tag, o, l in (("single", o1, l1), ("merged", o2, l2)):
+            og = to_np_f64(o[:, h:h + 1, rows])
+            lg = to_np_f64(l[:, h:h + 1, rows])
+            compare(og, lg, O_ref, L_ref, valid, f"wan720 h{h} {tag}")
+            assert_pad_rows(og, lg, valid, f"wan720 h{h} {tag}")
+
+
+@pytest.mark.parametrize("cuts", [[0, 64, 128, 320], [0, 10, 10, 200, 320], [0, 300, 320], [0, 1, 320]])
+def test_uneven_shards_and_empty_shard_merge(ops, cuts):
+    import torch
+    w = W.WORKLOADS["tiny"]
+    say(f"tiny shards {cuts}")
+    q, k, v = W.make_qkv(w)
+    pos = W.positions(w)
+    cos, sin = gpu_tables(ops, w)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    po, pl = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        kvv = max(0, min(w.s_valid - a, b - a))
+        # a shard view must start on a 16-byte boundary: copy odd cuts to fresh buffers
+        ks, vs = kd[:, :, a:b].contiguous(), vd[:, :, a:b].contiguous()
+        o, l = ops.attn_fwd(qd, ks, vs, q_valid=w.s_valid, kv_valid=kvv, rope_q=(cos, sin),
+                            rope_k=(cos[a:b].contiguous(), sin[a:b].contiguous()), out_dtype=torch.float32)
+        po.append(o)
+        pl.append(l)
+    om, lm = ops.lse_merge(po, pl, q_valid=w.s_valid)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
+    valid = np.arange(w.s_pad) < w.s_valid
+    og, lg = to_np_f64(om), to_np_f64(lm)
+    compare(og, lg, O_ref, L_ref, valid, f"tiny shards {cuts}")
+    assert_pad_rows(og, lg, valid, "shards")
+
+
+@pytest.mark.parametrize("part_dtype", ["f32", "bf16"])
+def test_merge_kernel_against_oracle(ops, part_dtype):
+    import torch
+    say(f"merge kernel {part_dtype}")
+    r = np.random.default_rng(31)
+    B, H, S, d, n = 1, 3, 200, 128, 5
+    Os = [r.standard_normal((B, H, S, d)).astype(np.float32) for _ in range(n)]
+    Ls = [(r.standard_normal((B, H, S)) * 4).astype(np.float32) for _ in range(n)]
+    Ls[2][:, :, :50] = -np.inf           # some rows empty in one part
+    for x in Ls:
+        x[:, 1, 60:70] = -np.inf         # rows empty in every part
+    tdt = torch.float32 if part_dtype == "f32" else torch.bfloat16
+    od = [torch.from_numpy(x).to(dev()).to(tdt) for x in Os]
+    ld = [torch.from_numpy(x).to(dev()) for x in Ls]
+    om, lm = ops.lse_merge(od, ld, q_valid=190, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Oin = [to_np_f64(x) for x in od]
+    O_ref, L_ref = oracle.lse_merge(Oin, [x.astype(np.float64) for x in Ls], q_valid=190)
+    og, lg = to_np_f64(om), to_np_f64(lm)
+    assert np.abs(og - O_ref).max() < 1e-5
+    fin = np.isfinite(L_ref)
+    assert np.array_equal(fin, np.isfinite(lg))
+    assert np.abs(lg[fin] - L_ref[fin]).max() < 1e-5
+    assert (og[:, 1, 60:70] == 0).all() and (og[:, :, 190:] == 0).all()
+
+
+# ------------------------------------------------------------------ edge cases
+def _edge(ops, seed, B, H, s_q, s_kv, d, q_valid, kv_valid, q_scale=1.0, rope=True):
+    import torch
+    r = np.random.default_rng(seed)
+    q = W.bf16_bits((r.standard_normal((B, H, s_q, d)) * q_scale).astype(np.float32))
+    k = W.bf16_bits(r.standard_normal((B, H, s_kv, d)).astype(np.float32))
+    v = W.bf16_bits(r.standard_normal((B, H, s_kv, d)).astype(np.float32))
+    k[:, :, kv_valid:] = W.finite_garbage_bits(r, k[:, :, kv_valid:].shape)
+    v[:, :, kv_valid:] = W.finite_garbage_bits(r, v[:, :, kv_valid:].shape)
+    pq = r.integers(0, 60, (s_q, 1)).astype(np.int32)
+    pk = r.integers(0, 60, (s_kv, 1)).astype(np.int32)
+    if rope:
+        tq = ops.rope_split_tables(torch.from_numpy(pq).to(dev()), (d,), d, 10000.0)
+        tk = ops.rope_split_tables(torch.from_numpy(pk).to(dev()), (d,), d, 10000.0)
+    else:
+        tq = tk = None
+    o, l = ops.attn_fwd(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), q_valid=q_valid, kv_valid=kv_valid,
+                        rope_q=tq, rope_k=tk)
+    torch.cuda.synchronize()
+    qf, kf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(k)
+    if rope:
+        O_ref, L_ref = oracle.dit_path(q, k, v, pq, pk, (d,), 10000.0, q_valid, kv_valid)
+        cq, sq = oracle.rope_tables(pq, (d,), 10000.0)
+        ck, sk = oracle.rope_tables(pk, (d,), 10000.0)
+        qf, kf = oracle.rope_split_halves(qf, cq, sq), oracle.rope_split_halves(kf, ck, sk)
+    else:
+        O_ref, L_ref = oracle.attention(qf, kf, oracle.bf16_to_f64(v), q_valid, kv_valid)
+    bound = lse_rounding_bound(qf, kf, kv_valid, 1.0 / math.sqrt(d))
+    # the oracle again on the rotated Q/K rounded to bf16 (the rounding the
+    # kernel documents): isolates the softmax / P.V arithmetic from it
+    rb = lambda x: oracle.bf16_to_f64(W.bf16_bits(x.astype(np.float32)))
+    O_rr, L_rr = oracle.attention(rb(qf), rb(kf), oracle.bf16_to_f64(v), q_valid, kv_valid)
+    _edge.rounded_ref = (O_rr, L_rr)
+    return to_np_f64(o), to_np_f64(l), O_ref, L_ref, bound
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=2, H=3, s_q=200, s_kv=77, d=128, q_valid=150, kv_valid=77),      # ragged, several tiles
+    dict(B=1, H=2, s_q=130, s_kv=320, d=64, q_valid=130, kv_valid=257),     # d=64, tail of one key
+    dict(B=1, H=1, s_q=64, s_kv=64, d=128, q_valid=64, kv_valid=1),         # one valid key
+    dict(B=1, H=2, s_q=256, s_kv=192, d=128, q_valid=1, kv_valid=192),      # one valid query
+    dict(B=1, H=2, s_q=300, s_kv=1000, d=128, q_valid=299, kv_valid=999, rope=False),
+])
+def test_edge_shapes(ops, case):
+    say(f"edge {case}")
+    c = dict(case)
+    rope = c.pop("rope", True)
+    og, lg, O_ref, L_ref, bound = _edge(ops, 41, rope=rope, **c)
+    valid = np.arange(c["s_q"]) < c["q_valid"]
+    # ungraded shapes: few keys leave the bf16 rounding of the rotated Q/K
+    # un-averaged in the LSE, so its tolerance is the derived rounding bound
+    compare(og, lg, O_ref, L_ref, valid, f"edge {case}", lse_tol=bound)
+    assert_pad_rows(og, lg, valid, "edge")
+
+
+def test_sharp_softmax_q_times_8(ops):
+    say("sharp softmax (Q x 8)")
+    og, lg, O_ref, L_ref, bound = _edge(ops, 43, 1, 4, 320, 320, 128, 300, 300, q_scale=8.0)
+    valid = np.arange(320) < 300
+    # scores ~ N(0, 64): the bf16 rounding of the rotated Q/K alone moves a
+    # score by up to ~0.4, so grade against the oracle on the rounded
+    # rotations, where a rescale error would still show as an O(|O|) miss
+    O_rr, L_rr = _edge.rounded_ref
+    res = compare(og, lg, O_rr, L_rr, valid, "sharp vs rounded-rotation oracle")
+    assert res["o_max_rel_to_rms"] < 0.02
+    # and against the unrounded oracle within the derived LSE bound
+    dl = np.abs(lg - L_ref)[:, :, valid]
+    assert (dl <= bound[:, :, valid]).all()
+
+
+def test_no_valid_keys_gives_zero_and_minus_inf(ops):
+    import torch
+    say("kv_valid = 0")
+    r = np.random.default_rng(44)
+    q = to_dev_bf16(W.bf16_bits(r.standard_normal((1, 2, 100, 128)).astype(np.float32)))
+    k = to_dev_bf16(W.finite_garbage_bits(r, (1, 2, 64, 128)))
+    o, l = ops.attn_fwd(q, k, k, q_valid=100, kv_valid=0)
+    torch.cuda.synchronize()
+    assert (to_np_f64(o) == 0).all() and np.isneginf(to_np_f64(l)).all()
+
+
+def test_pad_unpad_round_trip(ops):
+    import torch
+    say("pad/unpad")
+    r = np.random.default_rng(45)
+    for shape, s_pad in (((1, 4680, 10, 128), 4736), ((2, 37, 3), 48), ((1, 300, 5), 320)):
+        x = torch.from_numpy(r.standard_normal(shape).astype(np.float32)).to(dev()).to(torch.bfloat16)
+        p = ops.pad_tokens(x, s_pad)
+        u = ops.unpad_tokens(p, shape[1])
+        torch.cuda.synchronize()
+        assert torch.equal(u.view(torch.int16), x.view(torch.int16))
+        assert (p[:, shape[1]:].view(torch.int16) == 0).all()
+        ref = oracle.pad_tokens(to_np_f64(x), s_pad)
+        assert np.array_equal(to_np_f64(p), ref)
