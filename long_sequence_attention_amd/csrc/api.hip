@@ -92,6 +92,12 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   if ((rc = check_strides("v", st)) != DIT_OK) return rc;
   resolve_strides(d->o_stride, d->H, d->s_q, d->d, st);
   if ((rc = check_strides("o", st)) != DIT_OK) return rc;
+  // K/V rows are fetched through 32-bit buffer views of one head's rows
+  int64_t kst[3], vst[3];
+  resolve_strides(d->k_stride, d->H, d->s_kv, d->d, kst);
+  resolve_strides(d->v_stride, d->H, d->s_kv, d->d, vst);
+  if ((int64_t)d->kv_valid * kst[2] * 2 > 0x7fffffffLL || (int64_t)d->kv_valid * vst[2] * 2 > 0x7fffffffLL)
+    return fail(DIT_ERR_UNSUPPORTED, "kv_valid * row stride of K or V exceeds 2 GiB for one head");
   *scale_out = scale;
   return DIT_OK;
 }

@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 import workloads as W
-from helpers import (assert_pad_rows, compare, ensure_built, lse_rounding_bound, raw_bits, to_dev_bf16, to_np_f64)
+from helpers import (assert_pad_rows, compare, ensure_built, lse_rounding_bound, o_rounding_bound, raw_bits,
+                     to_dev_bf16, to_np_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -253,6 +254,7 @@ def _edge(ops, seed, B, H, s_q, s_kv, d, q_valid, kv_valid, q_scale=1.0, rope=Tr
     rb = lambda x: oracle.bf16_to_f64(W.bf16_bits(x.astype(np.float32)))
     O_rr, L_rr = oracle.attention(rb(qf), rb(kf), oracle.bf16_to_f64(v), q_valid, kv_valid)
     _edge.rounded_ref = (O_rr, L_rr)
+    _edge.v = oracle.bf16_to_f64(v[:, :, :kv_valid])
     return to_np_f64(o), to_np_f64(l), O_ref, L_ref, bound
 
 
@@ -283,8 +285,9 @@ def test_sharp_softmax_q_times_8(ops):
     # score by up to ~0.4, so grade against the oracle on the rounded
     # rotations, where a rescale error would still show as an O(|O|) miss
     O_rr, L_rr = _edge.rounded_ref
-    res = compare(og, lg, O_rr, L_rr, valid, "sharp vs rounded-rotation oracle")
-    assert res["o_max_rel_to_rms"] < 0.02
+    otol = o_rounding_bound(O_rr, _edge.v)
+    res = compare(og, lg, O_rr, L_rr, valid, "sharp vs rounded-rotation oracle", o_tol=otol)
+    assert res["o_max_rel_to_rms"] < 0.03
     # and against the unrounded oracle within the derived LSE bound
     dl = np.abs(lg - L_ref)[:, :, valid]
     assert (dl <= bound[:, :, valid]).all()
