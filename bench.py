@@ -83,10 +83,13 @@ def main():
     lse = torch.empty((B, H, Sp), dtype=torch.float32, device=dev)
     cos = torch.empty((Sp, d // 2), dtype=torch.float32, device=dev)
     sin = torch.empty_like(cos)
-    ws = torch.empty(B * H * Sp * d * 2 + 256, dtype=torch.uint8, device=dev)
     L = ops._native.lib()
     import ctypes
     chans = (ctypes.c_int32 * len(w.axes))(*w.axes)
+
+    qv, kv_, vv = qp.transpose(1, 2), kp.transpose(1, 2), vp.transpose(1, 2)
+    ws = torch.empty(ops.attn_workspace_size(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin)),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         s = ops._stream(dev)

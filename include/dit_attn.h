@@ -55,6 +55,15 @@ typedef enum {
 
 typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
 
+/* How dit_attn_fwd spreads work over the GPU (results agree to rounding;
+ * each schedule is bit-reproducible from call to call):
+ * AUTO currently resolves to PER_QTILE (one workgroup per 128-row query
+ * tile), which measures fastest on MI355X for the shapes tested.
+ * BALANCED gives every workgroup an equal run of (query tile, key tile)
+ * pairs; query tiles split between workgroups are combined in the
+ * workspace by the last workgroup to finish (no waiting between them). */
+typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED = 2 } dit_schedule;
+
 /*
  * Attention forward descriptor.
  *
@@ -85,9 +94,14 @@ typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
  * result that dit_lse_merge will combine), written for rows [0, s_q).
  * lse: fp32 dense [B, H, s_q], natural log, or NULL to skip it.
  *
- * workspace: device scratch for the once-per-call K rotation; required
- * (non-NULL, 256-byte aligned, at least dit_attn_workspace_size() bytes) when
- * cos_k/sin_k are given, ignored otherwise. The caller owns it.
+ * workspace: device scratch for the once-per-call K rotation and, under the
+ * BALANCED schedule, the partial results of split query tiles and their
+ * arrival counters. Required (non-NULL, 256-byte aligned, at least
+ * dit_attn_workspace_size() bytes) when that size is non-zero. The caller
+ * owns it; its contents need not be initialised. Calls that share one
+ * workspace must not overlap.
+ *
+ * schedule: a dit_schedule value (0 = AUTO).
  */
 typedef struct dit_attn_desc {
   int32_t B, H, d;               /* d in {64, 128}, else DIT_ERR_UNSUPPORTED */
@@ -103,9 +117,11 @@ typedef struct dit_attn_desc {
   const float *cos_k, *sin_k;    /* fp32 [s_kv, d/2] or NULL */
   void *workspace;
   size_t workspace_bytes;
+  int32_t schedule;              /* dit_schedule */
 } dit_attn_desc;
 
-/* Bytes of workspace dit_attn_fwd needs for `desc` (0 when K is not rotated). */
+/* Bytes of workspace dit_attn_fwd needs for `desc` on the current device
+ * (0 when K is not rotated and the schedule needs no partial results). */
 DIT_API int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes);
 
 /* Attention forward with fused RoPE and exact pad-key masking; see above. */

@@ -53,7 +53,7 @@ def plan_padding(s_valid: int, multiple: int) -> int:
     return out.value
 
 
-def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale):
+def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule=0):
     B, H, s_q, d = q.shape
     desc = N.AttnDesc()
     desc.B, desc.H, desc.d = B, H, d
@@ -69,27 +69,31 @@ def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale):
         desc.cos_q, desc.sin_q = rope_q[0].data_ptr(), rope_q[1].data_ptr()
     if rope_k is not None:
         desc.cos_k, desc.sin_k = rope_k[0].data_ptr(), rope_k[1].data_ptr()
+    desc.schedule = int(schedule)
     return desc
 
 
-def attn_workspace_size(q, k, v, *, kv_valid=None, rope_k=None) -> int:
-    """Workspace bytes attn_fwd needs (the once-per-call rotated K)."""
+def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, schedule=0) -> int:
+    """Workspace bytes attn_fwd needs (dit_attn_workspace_size) on q's device."""
+    q_valid = q.shape[2] if q_valid is None else int(q_valid)
     kv_valid = k.shape[2] if kv_valid is None else int(kv_valid)
-    if rope_k is None or kv_valid == 0:
-        return 0
-    B, H, s_kv, d = k.shape
-    return (B * H * s_kv * d * 2 + 255) // 256 * 256
+    desc = _attn_desc(q, k, v, q, None, q_valid, kv_valid, rope_q, rope_k, 0.0, schedule)
+    need = ctypes.c_size_t()
+    with torch.cuda.device(q.device):
+        N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_workspace_size")
+    return need.value
 
 
 def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
-             out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None):
+             out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None, schedule=0):
     """Attention forward (dit_attn_fwd).
 
     q: [B, H, s_q, d], k/v: [B, H, s_kv, d] bf16 device tensors, any strides
     with d contiguous (e.g. a permuted [B, S, H, d] buffer). Rows >= q_valid /
     kv_valid are tail pads. rope_q / rope_k: (cos, sin) fp32 [S, d/2] tables
-    or None. Returns (O, LSE) with O [B, H, s_q, d] in out_dtype (or `out`)
-    and LSE fp32 [B, H, s_q] (natural log), or O alone if return_lse=False.
+    or None. schedule: 0 auto, 1 one workgroup per query tile, 2 balanced.
+    Returns (O, LSE) with O [B, H, s_q, d] in out_dtype (or `out`) and LSE
+    fp32 [B, H, s_q] (natural log), or O alone if return_lse=False.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_cuda(name, t, torch.bfloat16)
@@ -116,9 +120,10 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
         _need_cuda("lse", lse, torch.float32)
         if lse.shape != (B, H, s_q) or not lse.is_contiguous():
             raise ValueError("lse must be contiguous fp32 [B, H, s_q]")
-    desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale)
+    desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule)
     need = ctypes.c_size_t()
-    N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")
+    with torch.cuda.device(q.device):
+        N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")
     if need.value:
         if workspace is None:
             workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
@@ -126,7 +131,8 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
             raise ValueError(f"workspace needs {need.value} bytes")
         desc.workspace = workspace.data_ptr()
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
-    N.check(N.lib().dit_attn_fwd(ctypes.byref(desc), _stream(q.device)), "attn_fwd")
+    with torch.cuda.device(q.device):
+        N.check(N.lib().dit_attn_fwd(ctypes.byref(desc), _stream(q.device)), "attn_fwd")
     return (out, lse) if return_lse else out
 
 

@@ -16,6 +16,9 @@ DIT_ERR_UNSUPPORTED = -2
 DIT_ERR_HIP = -3
 DIT_BF16 = 0
 DIT_F32 = 1
+DIT_SCHED_AUTO = 0
+DIT_SCHED_PER_QTILE = 1
+DIT_SCHED_BALANCED = 2
 
 EXPORTED = (
     "dit_attn_workspace_size",
@@ -46,6 +49,7 @@ class AttnDesc(ctypes.Structure):
         ("cos_k", ctypes.c_void_p), ("sin_k", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("schedule", ctypes.c_int32),
     ]
 
 

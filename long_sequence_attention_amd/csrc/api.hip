@@ -102,11 +102,62 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   return DIT_OK;
 }
 
-size_t attn_workspace_bytes(const dit_attn_desc *d) {
-  if (d->cos_k == nullptr || d->kv_valid == 0) return 0;
-  return round_up((size_t)d->B * d->H * (size_t)d->s_kv * d->d * 2, 256);
-}
+// Launch plan of one dit_attn_fwd call: K rotation and schedule, and where
+// their scratch lives inside the caller's workspace.
+struct AttnPlan {
+  size_t k_bytes = 0;       // rotated K, dense [B, H, s_kv, d] bf16
+  int groups = 0;           // balanced-schedule workgroups (0 = one per q-tile)
+  size_t part_o_off = 0, part_l_off = 0, count_off = 0, table_off = 0, owners_off = 0;
+  int64_t n_counts = 0;
+  size_t total = 0;
+};
 
+constexpr int kBlockM = 128, kBlockN = 64, kThreads = 256;
+
+int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
+  AttnPlan p;
+  if (d->cos_k != nullptr && d->kv_valid > 0) p.k_bytes = round_up((size_t)d->B * d->H * (size_t)d->s_kv * d->d * 2, 256);
+  const int64_t nq = (int64_t)d->B * d->H * ((d->s_q + kBlockM - 1) / kBlockM);
+  const int64_t nk = (d->kv_valid + kBlockN - 1) / kBlockN;
+  const int64_t units = nq * nk;
+  if (d->schedule < DIT_SCHED_AUTO || d->schedule > DIT_SCHED_BALANCED)
+    return fail(DIT_ERR_INVALID, "schedule=%d is not a dit_schedule", d->schedule);
+  // AUTO resolves to one workgroup per q-tile: on MI355X the balanced
+  // schedule measures no faster yet on the Wan / FLUX / HunyuanVideo shapes
+  // (its partial writes and merges cost what the idle tail of the last
+  // round of workgroups saves), so it runs only when asked for.
+  const bool may_balance = d->schedule == DIT_SCHED_BALANCED;
+  if (may_balance && units > 0 && nq > 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return fail(DIT_ERR_HIP, "cannot query the compute-unit count of the current device");
+    const int64_t slots = 2LL * cus;   // two 4-wave workgroups fit one CU
+    // whole rounds of slots, and at least as many workgroups as q-tiles so
+    // a workgroup's run of key tiles spans at most two q-tiles
+    int64_t g = slots * ((nq + slots - 1) / slots);
+    if (g > units / 4) g = units / 4;   // at least 4 key tiles per workgroup
+    if (g < nq) g = nq;
+    if (g > 65535) g = 65535;
+    p.groups = g >= nq ? (int)g : 0;
+  }
+  size_t off = p.k_bytes;
+  if (p.groups > 0) {
+    p.part_o_off = off;
+    off += round_up((size_t)2 * p.groups * kThreads * (d->d / 2) * sizeof(float), 256);
+    p.part_l_off = off;
+    off += round_up((size_t)2 * p.groups * kBlockM * sizeof(float), 256);
+    p.count_off = off;
+    p.n_counts = nq;
+    off += round_up((size_t)nq * sizeof(int32_t), 256);
+    p.table_off = off;
+    off += round_up((size_t)2 * p.groups * 4 * sizeof(int32_t), 256);
+    p.owners_off = off;
+    off += round_up((size_t)nq * 2 * sizeof(int32_t), 256);
+  }
+  p.total = off;
+  *pl = p;
+  return DIT_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -125,9 +176,11 @@ int dit_plan_padding(int s_valid, int multiple, int *s_pad_out) {
 int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes) {
   if (bytes == nullptr) return fail(DIT_ERR_INVALID, "bytes is NULL");
   float scale;
-  const int rc = validate_attn(desc, &scale);
+  int rc = validate_attn(desc, &scale);
   if (rc != DIT_OK) return rc;
-  *bytes = attn_workspace_bytes(desc);
+  AttnPlan pl;
+  if ((rc = plan_attn(desc, &pl)) != DIT_OK) return rc;
+  *bytes = pl.total;
   return ok();
 }
 
@@ -136,10 +189,12 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
   int rc = validate_attn(desc, &scale);
   if (rc != DIT_OK) return rc;
   const dit_attn_desc &d = *desc;
-  const size_t need = attn_workspace_bytes(desc);
+  AttnPlan pl;
+  if ((rc = plan_attn(desc, &pl)) != DIT_OK) return rc;
+  const size_t need = pl.total;
   if (need > 0) {
     if (d.workspace == nullptr || d.workspace_bytes < need)
-      return fail(DIT_ERR_INVALID, "workspace of %zu bytes required for the K rotation (got %zu)", need,
+      return fail(DIT_ERR_INVALID, "workspace of %zu bytes required (got %zu)", need,
                   d.workspace == nullptr ? (size_t)0 : d.workspace_bytes);
     if ((reinterpret_cast<uintptr_t>(d.workspace) & 255u) != 0) return fail(DIT_ERR_INVALID, "workspace must be 256-byte aligned");
   }
@@ -169,7 +224,7 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
   p.n_qtiles = (d.s_q + 127) / 128;
   p.scale_log2 = scale * 1.4426950408889634f;
 
-  if (need > 0) {
+  if (pl.k_bytes > 0) {
     dit::RopeRotateParams r{};
     r.x = p.k;
     r.y = static_cast<dit::bf16_t *>(d.workspace);
@@ -183,6 +238,20 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
     p.ks_b = (int64_t)d.H * d.s_kv * d.d;
     p.ks_h = (int64_t)d.s_kv * d.d;
     p.ks_s = d.d;
+  }
+  if (pl.groups > 0) {
+    char *ws = static_cast<char *>(d.workspace);
+    p.sk_groups = pl.groups;
+    p.sk_part_o = reinterpret_cast<float *>(ws + pl.part_o_off);
+    p.sk_part_l = reinterpret_cast<float *>(ws + pl.part_l_off);
+    p.sk_count = reinterpret_cast<int32_t *>(ws + pl.count_off);
+    int4 *table = reinterpret_cast<int4 *>(ws + pl.table_off);
+    int2 *owners = reinterpret_cast<int2 *>(ws + pl.owners_off);
+    p.sk_table = table;
+    p.sk_owners = owners;
+    rc = hip_status(dit::launch_sk_plan(table, owners, p.sk_count, pl.groups, (int)pl.n_counts,
+                                        (d.kv_valid + kBlockN - 1) / kBlockN, st), "schedule plan launch");
+    if (rc != DIT_OK) return rc;
   }
   return hip_status(dit::launch_attn_fwd(p, d.d, st), "attention launch");
 }

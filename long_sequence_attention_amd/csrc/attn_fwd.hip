@@ -56,6 +56,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 __device__ __forceinline__ u32x4 ldg16(const bf16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
@@ -99,33 +100,61 @@ struct Geo {
   __device__ static constexpr int fv(int r) { return 4 * ((r / RPB) % (4 / RPB)); }
 };
 
-// Issue this wave's share of tile t of K or V as buffer->LDS loads. The
-// buffer view starts at the tile's first row and ends at row kv_valid, so
-// rows past kv_valid (tail pads, or past the tensor) arrive as zeros. The
-// view is rebuilt per tile with scalar arithmetic: the hardware range check
-// covers the per-lane offset, not a scalar offset.
-template <int D>
-__device__ __forceinline__ void issue_rows(char *dst, const bf16_t *base, int row_bytes, int t, int kv_valid,
-                                           const int *off, int wave) {
+// One 16-byte-per-lane buffer load that writes LDS directly (lane l's 16
+// bytes land at M0 + 16 l). Issued as inline assembly so the compiler does
+// not treat it as a pending LDS write that every later LDS read must wait
+// for: the kernel orders these loads itself (s_waitcnt vmcnt(0) and a
+// barrier before a filled buffer is read). M0 = wbase + OFF is formed inside
+// the statement (one wait state before the load reads it), so the 16
+// distinct LDS targets of a step do not each hold an SGPR. No other code in
+// these kernels uses M0.
+template <int OFF>
+__device__ __forceinline__ void lds_dma16(uint32_t wbase, int voff, i32x4 rsrc) {
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(wbase), "v"(voff), "s"(rsrc), "i"(OFF)
+               : "memory", "scc");
+}
+
+// Issue this wave's share of tile t of K or V into LDS buffer BUF (byte
+// offset in the tile area) as buffer->LDS loads; wbase is the LDS address of
+// this wave's first 1 KB slot. The buffer view starts at the tile's first
+// row and ends at row kv_valid, so rows past kv_valid (tail pads, or past
+// the tensor) arrive as zeros. The view is rebuilt per tile with scalar
+// arithmetic: the hardware range check covers the per-lane offset, not a
+// scalar offset.
+template <int D, int BUF>
+__device__ __forceinline__ void issue_rows(uint32_t wbase, const bf16_t *base, int row_bytes, int t, int kv_valid,
+                                           const int *off) {
   using G = Geo<D>;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char *>(reinterpret_cast<const char *>(base)) + (int64_t)t * BN * row_bytes, 0,
-      (kv_valid - t * BN) * row_bytes, 0x00020000);
-#pragma unroll
-  for (int i = 0; i < G::LOADS_PER_WAVE; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + (wave * G::LOADS_PER_WAVE + i) * 1024), 16,
-                                             off[i], 0, 0, 0);
+  const uint64_t addr = reinterpret_cast<uint64_t>(base) + (uint64_t)((int64_t)t * BN * row_bytes);
+  // descriptor: base, stride 0, num_records = bytes to row kv_valid, raw buffer
+  const i32x4 rs = {(int32_t)(uint32_t)addr, (int32_t)((addr >> 32) & 0xffffu), (kv_valid - t * BN) * row_bytes,
+                    0x00020000};
+  if constexpr (G::LOADS_PER_WAVE > 0) lds_dma16<BUF + 0 * 1024>(wbase, off[0], rs);
+  if constexpr (G::LOADS_PER_WAVE > 1) lds_dma16<BUF + 1 * 1024>(wbase, off[1], rs);
+  if constexpr (G::LOADS_PER_WAVE > 2) lds_dma16<BUF + 2 * 1024>(wbase, off[2], rs);
+  if constexpr (G::LOADS_PER_WAVE > 3) lds_dma16<BUF + 3 * 1024>(wbase, off[3], rs);
+  static_assert(G::LOADS_PER_WAVE <= 4, "at most four 1 KB loads per wave and tile");
+}
+
+// Runtime buffer parity -> compile-time LDS offset.
+template <int D, int BUF0>
+__device__ __forceinline__ void issue_rows_par(int par, uint32_t wbase, const bf16_t *base, int row_bytes, int t,
+                                               int kv_valid, const int *off) {
+  if (par) issue_rows<D, BUF0 + Geo<D>::TILE_BYTES>(wbase, base, row_bytes, t, kv_valid, off);
+  else issue_rows<D, BUF0>(wbase, base, row_bytes, t, kv_valid, off);
 }
 
 template <int D>
-__device__ __forceinline__ void qk_tile(const char *kt, const int *kaddr, const bf16x8 *qop, f32x16 *sacc) {
+__device__ __forceinline__ void qk_tile(const char *kt, int kx, const bf16x8 *qop, f32x16 *sacc) {
   constexpr int DK = D / 16;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     sacc[blk] = f32x16{};
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + blk * 32 * D * 2 + kaddr[dk]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + blk * 32 * D * 2 + (kx ^ (32 * dk)));
       sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[dk], sacc[blk], 0, 0, 0);
     }
   }
@@ -158,28 +187,39 @@ __device__ __forceinline__ float pair_max(const f32x16 *s) {
 template <int D>
 struct StepCtx {
   char *smem;
+  uint32_t wbase;
   const bf16_t *kbase, *vbase;
-  const int *koff, *voff, *kaddr, *vaddr;
+  const int *koff, *voff;
+  int kx, vx;
   const bf16x8 *qop;
-  int ks_bytes, vs_bytes, kv_valid, n_tiles, wave, hf;
+  int ks_bytes, vs_bytes, kv_valid, t_end, wave, hf;
   float c2;
 };
 
-template <int D, bool HAS_NEXT, bool MASK_NEXT>
-__device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, const f32x16 *scur, f32x16 *snext,
-                                     f32x16 *acc_o, float &m_run, float &l_run) {
+// One key tile of the main loop. Block A: P(t) = exp2(S(t) - m) on VALU while
+// S(t+1) = K(t+1) Q^T runs on MFMA; block B: O^T += V(t)^T P(t)^T on MFMA
+// while the row max of S(t+1) is taken. Then the (rare) lazy rescale.
+// par is the LDS buffer parity of tile t within the current key range.
+// STEADY: tile t+1 exists and is full, parity static, scheduled with
+// sched_group_barrier. Otherwise has_next / mask_next are run-time flags
+// (the last tiles of a run) and the next scores are copied into scur.
+template <int D, bool STEADY>
+__device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x16 *scur, f32x16 *snext,
+                                     f32x16 *acc_o, float &m_run, float &l_run, bool has_next = true,
+                                     bool mask_next = false) {
+  const bool HAS_NEXT = STEADY || has_next;
   using G = Geo<D>;
+  const int kx = cx.kx, vx = cx.vx;
   constexpr int DK = D / 16, DB = D / 32;
-  if (t + 2 < cx.n_tiles)
-    issue_rows<D>(cx.smem + G::K0 + par * G::TILE_BYTES, cx.kbase, cx.ks_bytes, t + 2, cx.kv_valid, cx.koff, cx.wave);
+  if (t + 2 < cx.t_end)
+    issue_rows_par<D, G::K0>(par, cx.wbase, cx.kbase, cx.ks_bytes, t + 2, cx.kv_valid, cx.koff);
   if (HAS_NEXT)
-    issue_rows<D>(cx.smem + G::V0 + (par ^ 1) * G::TILE_BYTES, cx.vbase, cx.vs_bytes, t + 1, cx.kv_valid, cx.voff, cx.wave);
+    issue_rows_par<D, G::V0>(par ^ 1, cx.wbase, cx.vbase, cx.vs_bytes, t + 1, cx.kv_valid, cx.voff);
   const char *vt = cx.smem + G::V0 + par * G::TILE_BYTES;
 
   const float neg_m = -m_run;
   bf16x8 pop[2][2];
   float ps0 = 0.f, ps1 = 0.f;
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
@@ -196,8 +236,8 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, const
     }
   }
   if (HAS_NEXT) {
-    qk_tile<D>(cx.smem + G::K0 + (par ^ 1) * G::TILE_BYTES, cx.kaddr, cx.qop, snext);
-    if (MASK_NEXT) mask_tail(snext, (t + 1) * BN, cx.kv_valid, cx.hf);
+    qk_tile<D>(cx.smem + G::K0 + (par ^ 1) * G::TILE_BYTES, kx, cx.qop, snext);
+    if (!STEADY && mask_next) mask_tail(snext, (t + 1) * BN, cx.kv_valid, cx.hf);
   }
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
@@ -205,7 +245,7 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, const
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const char *src = vt + (blk * 32 + a * 16) * D * 2 + cx.vaddr[db];
+        const char *src = vt + (blk * 32 + a * 16) * D * 2 + (vx ^ (64 * db));
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(src));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(src + 4 * D * 2));
         const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -215,7 +255,7 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, const
   }
   float mts = 0.f;
   if (HAS_NEXT) mts = pair_max(snext) * cx.c2;
-  if (HAS_NEXT && !MASK_NEXT) {
+  if (STEADY) {
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < 2 * DK; ++i) {
@@ -243,66 +283,57 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, const
       for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
       m_run = m_new;
     }
+    if (!STEADY) {
+      scur[0] = snext[0];
+      scur[1] = snext[1];
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 }
 
+// Per-workgroup state that does not depend on which q-tile is processed.
 template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
+struct Lane {
+  int tid, lane, wave, l32, hf;
+  int ks_bytes, vs_bytes;
+  int koff[Geo<D>::LOADS_PER_WAVE], voff[Geo<D>::LOADS_PER_WAVE];
+  int kx, vx;   // operand read offsets of d-chunk 0 (see the kernel prologue)
+};
+
+// Attention of one q-tile (128 rows of head bh) over key tiles [kb, ke).
+// On return acc_o holds this lane's unnormalised O^T (query qrow), m_run the
+// running max (log2 units, scaled) and l_run this lane's half of the row sum.
+template <int D, class P>
+__device__ __forceinline__ void run_qtile(const P &p, char *smem, const Lane<D> &ln, int b, int h, int qt,
+                                          int kb, int ke, f32x16 *acc_o, float &m_run, float &l_run) {
   using G = Geo<D>;
-  constexpr int DK = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int CPR = G::CPR;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * G::TILE_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hf = lane >> 5;
-
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = logical % p.n_qtiles;
-  const int bh = logical / p.n_qtiles;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
-
+  constexpr int DK = D / 16, DB = D / 32;
   const bf16_t *qbase = p.q + b * p.qs_b + h * p.qs_h;
   const bf16_t *kbase = p.k + b * p.ks_b + h * p.ks_h;
   const bf16_t *vbase = p.v + b * p.vs_b + h * p.vs_h;
   const int kv_valid = p.kv_valid;
-  const int n_tiles = (kv_valid + BN - 1) / BN;
 
-  const int ks_bytes = (int)(p.ks_s * 2), vs_bytes = (int)(p.vs_s * 2);
+  const uint32_t wbase = (uint32_t)(uintptr_t)(lds_void_t *)smem + ln.wave * G::LOADS_PER_WAVE * 1024;
+  issue_rows<D, G::K0>(wbase, kbase, ln.ks_bytes, kb, kv_valid, ln.koff);
+  issue_rows<D, G::V0>(wbase, vbase, ln.vs_bytes, kb, kv_valid, ln.voff);
+  if (kb + 1 < ke) issue_rows<D, G::K0 + G::TILE_BYTES>(wbase, kbase, ln.ks_bytes, kb + 1, kv_valid, ln.koff);
 
-  int koff[G::LOADS_PER_WAVE], voff[G::LOADS_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < G::LOADS_PER_WAVE; ++i) {
-    const int s = (wave * G::LOADS_PER_WAVE + i) * 64 + lane;
-    const int r = s / CPR, pos = s % CPR;
-    koff[i] = r * ks_bytes + ((pos ^ G::fk(r)) * 16);
-    voff[i] = r * vs_bytes + ((pos ^ G::fv(r)) * 16);
-  }
-  if (n_tiles > 0) {
-    issue_rows<D>(smem + G::K0, kbase, ks_bytes, 0, kv_valid, koff, wave);
-    issue_rows<D>(smem + G::V0, vbase, vs_bytes, 0, kv_valid, voff, wave);
-  }
-  if (n_tiles > 1) issue_rows<D>(smem + G::K0 + G::TILE_BYTES, kbase, ks_bytes, 1, kv_valid, koff, wave);
-
-  const int qrow = qt * BM + wave * 32 + l32;
+  // ---- Q operand (B of S^T): lane holds query qrow, d = dk*16 + hf*8 + e.
+  const int qrow = qt * BM + ln.wave * 32 + ln.l32;
   bf16x8 qop[DK];
   {
     u32x4 raw[DK];
     const bool in_q = qrow < p.s_q;
     const bf16_t *qr = qbase + (int64_t)(in_q ? qrow : 0) * p.qs_s;
 #pragma unroll
-    for (int dk = 0; dk < DK; ++dk) raw[dk] = in_q ? ldg16(qr + dk * 16 + hf * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int dk = 0; dk < DK; ++dk) raw[dk] = in_q ? ldg16(qr + dk * 16 + ln.hf * 8) : u32x4{0u, 0u, 0u, 0u};
     if (p.cos_q != nullptr) {
+      // pair (i, i + D/2) lives in (dk, dk + DK/2) of the same lane
       const int64_t trow = (int64_t)(in_q ? qrow : 0) * (D / 2);
 #pragma unroll
       for (int dk = 0; dk < DK / 2; ++dk) {
-        const int i0 = dk * 16 + hf * 8;
+        const int i0 = dk * 16 + ln.hf * 8;
         rotate8(raw[dk], raw[dk + DK / 2], p.cos_q + trow + i0, p.sin_q + trow + i0);
       }
     }
@@ -310,67 +341,46 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
     for (int dk = 0; dk < DK; ++dk) qop[dk] = __builtin_bit_cast(bf16x8, raw[dk]);
   }
 
-  const int kperm = (l32 & 16) + ((l32 & 4) << 1) + ((l32 & 8) >> 1) + (l32 & 3);
-  int kaddr[DK];
-#pragma unroll
-  for (int dk = 0; dk < DK; ++dk)
-    kaddr[dk] = kperm * (D * 2) + (((2 * dk + hf) ^ G::fk(kperm)) * 16);
-  const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
-  const int vrow = 8 * (tg >> 1) + te;
-  int vaddr[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int chunk = 4 * db + 2 * (tg & 1) + (tq >> 1);
-    vaddr[db] = vrow * (D * 2) + ((chunk ^ G::fv(vrow)) * 16) + 8 * (tq & 1);
-  }
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x16 acc_o[DB];
+  l_run = 0.f;
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
-
   const float c2 = p.scale_log2;
   f32x16 sa[2], sb[2];
-  if (n_tiles > 0) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    qk_tile<D>(smem + G::K0, kaddr, qop, sa);
-    __syncthreads();
-    if (BN > kv_valid) mask_tail(sa, 0, kv_valid, hf);
-    m_run = pair_max(sa) * c2;
-  }
-  StepCtx<D> cx{smem, kbase, vbase, koff, voff, kaddr, vaddr, qop, ks_bytes, vs_bytes, kv_valid, n_tiles, wave, hf, c2};
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K(kb), V(kb), K(kb+1) landed
+  __syncthreads();
+  qk_tile<D>(smem + G::K0, ln.kx, qop, sa);
+  __syncthreads();                      // K(kb)'s buffer is refilled by the first step
+  if ((kb + 1) * BN > kv_valid) mask_tail(sa, kb * BN, kv_valid, ln.hf);
+  m_run = pair_max(sa) * c2;            // first tile: nothing accumulated yet
+
+  StepCtx<D> cx{smem, wbase, kbase, vbase, ln.koff, ln.voff, ln.kx, ln.vx, qop,
+                ln.ks_bytes, ln.vs_bytes, kv_valid, ke, ln.wave, ln.hf, c2};
   // steady state: tiles t, t+1, t+2 all full; two tiles per iteration so the
   // score registers alternate roles and the LDS buffer parity is static
-  int t = 0;
-  for (; t + 3 < n_tiles; t += 2) {
-    step<D, true, false>(cx, t, 0, sa, sb, acc_o, m_run, l_run);
-    step<D, true, false>(cx, t + 1, 1, sb, sa, acc_o, m_run, l_run);
+  int t = kb;
+  for (; t + 3 < ke; t += 2) {
+    step<D, true>(cx, t, 0, sa, sb, acc_o, m_run, l_run);
+    step<D, true>(cx, t + 1, 1, sb, sa, acc_o, m_run, l_run);
   }
-  // at most three tiles remain (t is even here): tile t+1 may be the masked tail
-  if (t + 1 < n_tiles) {
-    if ((t + 2) * BN > kv_valid) step<D, true, true>(cx, t, 0, sa, sb, acc_o, m_run, l_run);
-    else step<D, true, false>(cx, t, 0, sa, sb, acc_o, m_run, l_run);
-    ++t;
-    if (t + 1 < n_tiles) {
-      if ((t + 2) * BN > kv_valid) step<D, true, true>(cx, t, 1, sb, sa, acc_o, m_run, l_run);
-      else step<D, true, false>(cx, t, 1, sb, sa, acc_o, m_run, l_run);
-      ++t;
-      step<D, false, false>(cx, t, 0, sa, sb, acc_o, m_run, l_run);
-    } else {
-      step<D, false, false>(cx, t, 1, sb, sa, acc_o, m_run, l_run);
-    }
-  } else if (t < n_tiles) {
-    step<D, false, false>(cx, t, 0, sa, sb, acc_o, m_run, l_run);
+  // the last (at most three) tiles: run-time flags; tile t+1 may be the
+  // masked tail
+  for (; t < ke; ++t) {
+    const bool has_next = t + 1 < ke;
+    step<D, false>(cx, t, (t - kb) & 1, sa, sb, acc_o, m_run, l_run, has_next, has_next && (t + 2) * BN > kv_valid);
   }
+}
 
-  // ---- epilogue: O = acc / l; LSE = (m + log2 l) ln 2; pad rows by select
-  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// Final epilogue: O = acc / l; LSE = (m + log2 l) ln 2; pad rows by select.
+template <int D, class P>
+__device__ __forceinline__ void store_final(const P &p, int b, int h, int qrow, int hf, const f32x16 *acc_o,
+                                            float lse2, float inv_l, bool row_ok) {
+  constexpr int DB = D / 32;
   if (qrow >= p.s_q) return;
-  const bool row_ok = (qrow < p.q_valid) && (kv_valid > 0);
-  const float inv = row_ok ? 1.0f / l_tot : 0.0f;
   const int64_t obase = b * p.os_b + h * p.os_h + (int64_t)qrow * p.os_s;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
       const int d0 = db * 32 + 8 * i + 4 * hf;
       float o4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o4[j] = row_ok ? acc_o[db][4 * i + j] * inv : 0.0f;
+      for (int j = 0; j < 4; ++j) o4[j] = row_ok ? acc_o[db][4 * i + j] * inv_l : 0.0f;
       if (p.o_f32) {
         float *op = reinterpret_cast<float *>(p.o) + obase + d0;
         *reinterpret_cast<float4 *>(op) = make_float4(o4[0], o4[1], o4[2], o4[3]);
@@ -389,9 +399,251 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
       }
     }
   }
-  if (p.lse != nullptr && hf == 0) {
-    const float lse = row_ok ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    p.lse[((int64_t)b * p.H + h) * p.s_q + qrow] = lse;
+  if (p.lse != nullptr && hf == 0) p.lse[((int64_t)b * p.H + h) * p.s_q + qrow] = row_ok ? lse2 * kLn2 : -INFINITY;
+}
+
+// Balanced schedule: workgroup w owns units [begin(w), begin(w+1)) of the
+// (q-tile, key-tile) space, q-tile major.
+__device__ __forceinline__ int64_t sk_begin(int64_t w, int64_t units, int groups) { return w * units / groups; }
+
+__device__ __forceinline__ int sk_owner(int64_t u, int64_t units, int groups) {
+  int64_t w = (u * groups) / units;
+  while (w + 1 < groups && sk_begin(w + 1, units, groups) <= u) ++w;
+  while (w > 0 && sk_begin(w, units, groups) > u) --w;
+  return (int)w;
+}
+
+// Partials of split q-tiles move between workgroups that may sit on
+// different XCDs (separate L2s), so they are written and read with the
+// agent-coherent cache policy (sc1) instead of through a fence that would
+// write back a whole L2. Slot s holds 256 threads x (d/8) float4 of O / l,
+// stored chunk-major so one wave instruction covers 1 KB contiguously, and
+// 128 floats of log2 LSE.
+constexpr int kSC1 = 16;   // buffer cache-policy bit: agent-coherent access
+
+template <int D, class P>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_o_view(const P &p, int slot) {
+  constexpr int BYTES = NT * D * 2;   // NT threads x (D/2) floats
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char *>(p.sk_part_o) + (int64_t)slot * BYTES, 0, BYTES,
+                                           0x00020000);
+}
+
+template <class P>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_l_view(const P &p, int slot) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char *>(p.sk_part_l) + (int64_t)slot * BM * 4, 0, BM * 4,
+                                           0x00020000);
+}
+
+template <class P>
+__device__ __forceinline__ int sk_slot(const P &p, int x, int T) {
+  return 2 * x + (p.sk_table[2 * x].x == T ? 0 : 1);
+}
+
+// The last piece of q-tile T to finish combines all pieces (written by
+// workgroups own.x..own.y; its own one is still in registers as the
+// normalised o = acc / l with log2 LSE lse2) and writes the final O and LSE:
+// O = sum_x w_x o_x / sum_x w_x with w_x = 2^(lse_x - M), M = max_x lse_x.
+// The pieces are combined in workgroup order whichever of them finished
+// last, so the result is the same bits on every call.
+template <int D, class P>
+__device__ __forceinline__ void merge_pieces(const P &p, const Lane<D> &ln, int T, int own_slot, int b, int h,
+                                             int qrow, bool row_ok, const f32x16 *o, float lse2) {
+  constexpr int DB = D / 32;
+  const int2 own = p.sk_owners[T];
+  const int row = ln.wave * 32 + ln.l32;
+  float M = -INFINITY;
+  for (int x = own.x; x <= own.y; ++x) {
+    const int sx = sk_slot(p, x, T);
+    const float lx =
+        sx == own_slot ? lse2 : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, sx), row * 4, 0, kSC1));
+    M = fmaxf(M, lx);
+  }
+  float wsum = 0.f;
+  for (int x = own.x; x <= own.y; ++x) {
+    const int sx = sk_slot(p, x, T);
+    wsum += __builtin_amdgcn_exp2f(
+        (sx == own_slot ? lse2 : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, sx), row * 4, 0, kSC1))) - M);
+  }
+  // one 32-channel block at a time, in place over o: the running sum of
+  // the pieces before this workgroup's own one needs only 16 registers
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    f32x16 a = f32x16{};
+    for (int x = own.x; x <= own.y; ++x) {
+      const int sx = sk_slot(p, x, T);
+      if (sx == own_slot) {
+        const float wx = __builtin_amdgcn_exp2f(lse2 - M);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = fmaf(wx, o[db][r], a[r]);
+      } else {
+        const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, sx);
+        const float wx = __builtin_amdgcn_exp2f(
+            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, sx), row * 4, 0, kSC1)) - M);
+        u32x4 c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(v, ln.tid * 16, (db * 4 + i) * NT * 16, kSC1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[4 * i + e] = fmaf(wx, __uint_as_float(c[i][e]), a[4 * i + e]);
+      }
+    }
+    acc[db] = a;
+  }
+  store_final<D>(p, b, h, qrow, ln.hf, acc, M + __log2f(wsum), row_ok ? 1.0f / wsum : 0.f, row_ok);
+}
+
+// Per-lane constants: wave / lane ids, the DMA source offsets and the
+// operand read offsets.
+template <int D, class P>
+__device__ __forceinline__ void make_lane(const P &p, int tid, Lane<D> &ln) {
+  using G = Geo<D>;
+  constexpr int CPR = G::CPR;
+  ln.tid = tid;
+  ln.lane = ln.tid & 63;
+  ln.wave = __builtin_amdgcn_readfirstlane(ln.tid >> 6);
+  ln.l32 = ln.lane & 31;
+  ln.hf = ln.lane >> 5;
+  ln.ks_bytes = (int)(p.ks_s * 2);
+  ln.vs_bytes = (int)(p.vs_s * 2);
+  // Per-lane source offsets for the wave's share of a tile: load i of wave w
+  // fills LDS slots s = (w*LPW + i)*64 + lane (16 bytes each), i.e. row
+  // s / CPR, position s % CPR, which holds chunk (position ^ f(row)).
+#pragma unroll
+  for (int i = 0; i < G::LOADS_PER_WAVE; ++i) {
+    const int s = (ln.wave * G::LOADS_PER_WAVE + i) * 64 + ln.lane;
+    const int r = s / CPR, pos = s % CPR;
+    ln.koff[i] = r * ln.ks_bytes + ((pos ^ G::fk(r)) * 16);
+    ln.voff[i] = r * ln.vs_bytes + ((pos ^ G::fv(r)) * 16);
+  }
+  // K operand: MFMA row m = l32 of block blk holds key blk*32 + kperm
+  const int kperm = (ln.l32 & 16) + ((ln.l32 & 4) << 1) + ((ln.l32 & 8) >> 1) + (ln.l32 & 3);
+  // chunk 2*dk + hf of row kperm sits at position (2*dk + hf) ^ fk(kperm);
+  // the row offset and (hf ^ fk) * 16 occupy bits disjoint from 32 * dk, so
+  // the offset for d-chunk dk is kx ^ (32 * dk)
+  ln.kx = kperm * (D * 2) + ((ln.hf ^ G::fk(kperm)) * 16);
+  // V operand via transpose reads: lane 16g + 4e + q points at
+  // V[base + 8*(g>>1) + e][db*32 + 16*(g&1) + 4q]
+  {
+    const int tg = ln.lane >> 4, te = (ln.lane >> 2) & 3, tq = ln.lane & 3;
+    const int vrow = 8 * (tg >> 1) + te;
+    // chunk 4*db + c0 (c0 < 4) sits at position chunk ^ fv(vrow), fv a
+    // multiple of 4, so the offset for channel block db is vx ^ (64 * db)
+    const int chunk0 = 2 * (tg & 1) + (tq >> 1);
+    ln.vx = vrow * (D * 2) + ((chunk0 ^ G::fv(vrow)) * 16) + 8 * (tq & 1);
+  }
+
+}
+
+// The kernel's AttnParams argument (the first explicit argument, at offset 0
+// of the kernel-argument segment) through a pointer the compiler cannot
+// track, so the fields a phase reads are loaded again with scalar loads
+// instead of being kept live in SGPRs from an earlier read.
+typedef const __attribute__((address_space(4))) AttnParams kernarg_params_t;
+__device__ __forceinline__ kernarg_params_t &kernarg_params() {
+  kernarg_params_t *kp = (kernarg_params_t *)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return *kp;
+}
+
+template <int D, bool BALANCED>
+__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
+  using G = Geo<D>;
+  constexpr int DK = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int CPR = G::CPR;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * G::TILE_BYTES];
+  __shared__ int last_flag;
+
+  Lane<D> ln;
+  make_lane<D>(p, threadIdx.x, ln);
+
+  const int kv_valid = p.kv_valid;
+  const int nk = (kv_valid + BN - 1) / BN;
+  f32x16 acc_o[DB];
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (!BALANCED) {
+    // one workgroup per q-tile, all key tiles
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = logical % p.n_qtiles;
+    const int bh = logical / p.n_qtiles;
+    const int h = bh % p.H, b = bh / p.H;
+    const int qrow = qt * BM + ln.wave * 32 + ln.l32;
+    if (nk > 0) {
+      run_qtile<D>(p, smem, ln, b, h, qt, 0, nk, acc_o, m_run, l_run);
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
+    }
+    const float l_tot = pair_sum(l_run);
+    const bool row_ok = (qrow < p.q_valid) && (nk > 0);
+    store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
+    return;
+  }
+
+  // ---- balanced schedule: this workgroup's one or two runs of key tiles,
+  // from the table the planning kernel wrote; q-tiles split between
+  // workgroups are combined by the last piece to finish.
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+#pragma unroll 1
+  for (int seg = 0; seg < 2; ++seg) {
+    // Parameters are re-read from the kernel-argument segment through an
+    // opaque pointer in each phase, and the per-lane constants rebuilt from
+    // an opaque thread id, so nothing but the loop counter stays live in
+    // registers across a run's key loop (SGPR pressure otherwise defeats the
+    // MFMA/VALU interleave of the steady state).
+    kernarg_params_t &pa = kernarg_params();
+    const int4 sg = pa.sk_table[2 * w + seg];   // {q-tile, kb, ke, slot or -1 when the run covers the q-tile}
+    if (sg.x < 0) break;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    make_lane<D>(pa, tid, ln);
+    {
+      const int qt = sg.x % pa.n_qtiles, bh = sg.x / pa.n_qtiles;
+      run_qtile<D>(pa, smem, ln, bh / pa.H, bh % pa.H, qt, sg.y, sg.z, acc_o, m_run, l_run);
+    }
+    kernarg_params_t &pe = kernarg_params();
+    const int4 se = pe.sk_table[2 * w + seg];
+    const int T = se.x, slot = se.w;
+    const int qt = T % pe.n_qtiles, bh = T / pe.n_qtiles;
+    const int h = bh % pe.H, b = bh / pe.H;
+    const int qrow = qt * BM + ln.wave * 32 + ln.l32;
+    const float l_tot = pair_sum(l_run);
+    const float lse2 = m_run + __log2f(l_tot);
+    const bool row_ok = qrow < pe.q_valid;
+    if (slot < 0) {
+      store_final<D>(pe, b, h, qrow, ln.hf, acc_o, lse2, row_ok ? 1.0f / l_tot : 0.f, row_ok);
+    } else {
+      // partial: O / l (fp32, in this lane's accumulator layout) and log2
+      // LSE, written agent-coherent; the arrival counter is bumped once
+      // every thread's stores completed.
+      const float inv = 1.0f / l_tot;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] *= inv;
+      const __amdgpu_buffer_rsrc_t v = part_o_view<D>(pe, slot);
+#pragma unroll
+      for (int j = 0; j < DB * 4; ++j) {
+        const int db = j >> 2, r = 4 * (j & 3);
+        const u32x4 c = {__float_as_uint(acc_o[db][r]), __float_as_uint(acc_o[db][r + 1]),
+                         __float_as_uint(acc_o[db][r + 2]), __float_as_uint(acc_o[db][r + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(c, v, ln.tid * 16, j * NT * 16, kSC1);
+      }
+      if (ln.hf == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), part_l_view(pe, slot), (ln.wave * 32 + ln.l32) * 4, 0, kSC1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial is in coherent memory
+      __syncthreads();
+      if (ln.tid == 0) {
+        const int2 own = pe.sk_owners[T];     // workgroups owning the pieces of q-tile T
+        const int old = __hip_atomic_fetch_add(pe.sk_count + T, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (old == own.y - own.x) ? 1 : 0;
+        if (last_flag) __hip_atomic_store(pe.sk_count + T, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (last_flag) merge_pieces<D>(pe, ln, T, slot, b, h, qrow, row_ok, acc_o, lse2);
+    }
+    __syncthreads();   // LDS and last_flag are reused by the next run
   }
 }
 
@@ -418,15 +670,57 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
   }
 }
 
+// Balanced-schedule plan: workgroup w owns units [begin(w), begin(w+1)) of
+// the (q-tile, key-tile) space, q-tile major, with begin(w) = w*units/groups.
+// Writes each workgroup's (at most two) runs, each q-tile's owner range,
+// partial slots (2w for a workgroup's first run, 2w+1 for its last), and
+// zeroes the arrival counters.
+__global__ __launch_bounds__(256) void sk_plan_kernel(int4 *table, int2 *owners, int32_t *count, int groups,
+                                                      int n_qt, int nk) {
+  const int64_t units = (int64_t)n_qt * nk;
+  for (int w = blockIdx.x * blockDim.x + threadIdx.x; w < groups; w += gridDim.x * blockDim.x) {
+    const int64_t u0 = sk_begin(w, units, groups), u1 = sk_begin(w + 1, units, groups);
+    // groups >= n_qt, so a run is at most one q-tile long and a workgroup
+    // has at most two runs; a run covering its whole q-tile needs no slot
+    int4 r[2] = {make_int4(-1, 0, 0, -1), make_int4(-1, 0, 0, -1)};
+    int n = 0;
+    for (int64_t u = u0; u < u1 && n < 2; ++n) {
+      const int T = (int)(u / nk), kb = (int)(u % nk);
+      const int ke = (int)((u1 - u < (int64_t)(nk - kb)) ? kb + (u1 - u) : nk);
+      const bool full = (kb == 0 && ke == nk);
+      r[n] = make_int4(T, kb, ke, full ? -1 : 2 * w + n);
+      u += ke - kb;
+    }
+    table[2 * w] = r[0];
+    table[2 * w + 1] = r[1];
+  }
+  for (int T = blockIdx.x * blockDim.x + threadIdx.x; T < n_qt; T += gridDim.x * blockDim.x) {
+    owners[T] = make_int2(sk_owner((int64_t)T * nk, units, groups), sk_owner((int64_t)(T + 1) * nk - 1, units, groups));
+    count[T] = 0;
+  }
+}
+
 }  // namespace
 
+hipError_t launch_sk_plan(int4 *table, int2 *owners, int32_t *count, int groups, int n_qt, int nk,
+                          hipStream_t stream) {
+  const int n = groups > n_qt ? groups : n_qt;
+  int blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(sk_plan_kernel, dim3(blocks), dim3(256), 0, stream, table, owners, count, groups, n_qt, nk);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream) {
-  const int64_t nblocks = (int64_t)p.n_qtiles * p.H * p.B;
+  const int64_t nblocks = p.sk_groups > 0 ? (int64_t)p.sk_groups : (int64_t)p.n_qtiles * p.H * p.B;
   if (nblocks <= 0) return hipSuccess;
+  const bool bal = p.sk_groups > 0;
   if (d == 128) {
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
+    if (bal) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
+    if (bal) hipLaunchKernelGGL((attn_fwd_kernel<64, true>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
   }
   return hipGetLastError();
 }

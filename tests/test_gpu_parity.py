@@ -317,3 +317,64 @@ def test_pad_unpad_round_trip(ops):
         assert (p[:, shape[1]:].view(torch.int16) == 0).all()
         ref = oracle.pad_tokens(to_np_f64(x), s_pad)
         assert np.array_equal(to_np_f64(p), ref)
+
+
+# ------------------------------------------------------------------ schedules
+@pytest.mark.parametrize("case", [
+    dict(name="tiny", sched=2),
+    dict(name="hunyuan", sched=2),
+    dict(name="wan480", sched=1),
+    dict(name="flux", sched=1),
+])
+def test_forced_schedules_match_oracle(ops, case):
+    """Both work schedules (one workgroup per query tile; balanced runs of
+    key tiles with split tiles combined in the workspace) against the oracle."""
+    import torch
+    w = W.WORKLOADS[case["name"]]
+    say(f"schedule {case['sched']} {w.name}")
+    q, k, v = W.make_qkv(w)
+    pos = W.positions(w)
+    tabs = gpu_tables(ops, w)
+    o, l = ops.attn_fwd(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), q_valid=w.s_valid, kv_valid=w.s_valid,
+                        rope_q=tabs, rope_k=tabs, schedule=case["sched"])
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
+    valid = np.arange(w.s_pad) < w.s_valid
+    og, lg = to_np_f64(o), to_np_f64(l)
+    compare(og, lg, O_ref, L_ref, valid, f"{w.name} schedule {case['sched']}")
+    assert_pad_rows(og, lg, valid, "schedule")
+
+
+@pytest.mark.parametrize("kv_valid", [1000, 999, 129, 65])
+def test_balanced_schedule_edge_key_counts(ops, kv_valid):
+    """Balanced schedule with ragged key counts: pieces that end on the masked
+    tail tile, single-tile pieces, and repeated calls reusing one workspace
+    (arrival counters are reset by every call)."""
+    import torch
+    say(f"balanced kv_valid={kv_valid}")
+    og, lg, O_ref, L_ref, bound = _edge(ops, 47, 1, 3, 384, 1024, 128, 380, kv_valid)
+    valid = np.arange(384) < 380
+    compare(og, lg, O_ref, L_ref, valid, f"per-qtile kv={kv_valid}", lse_tol=bound)
+    r = np.random.default_rng(47)
+    q = W.bf16_bits(r.standard_normal((1, 3, 384, 128)).astype(np.float32))
+    k = W.bf16_bits(r.standard_normal((1, 3, 1024, 128)).astype(np.float32))
+    v = W.bf16_bits(r.standard_normal((1, 3, 1024, 128)).astype(np.float32))
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    o1, l1 = ops.attn_fwd(qd, kd, vd, q_valid=380, kv_valid=kv_valid, schedule=1)
+    nbytes = ops.attn_workspace_size(qd, kd, vd, q_valid=380, kv_valid=kv_valid, schedule=2)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=dev())   # garbage, not zeros
+    outs = []
+    for _ in range(3):
+        o2, l2 = ops.attn_fwd(qd, kd, vd, q_valid=380, kv_valid=kv_valid, schedule=2, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((raw_bits(o2), raw_bits(l2)))
+    for a in outs[1:]:
+        assert np.array_equal(a[0], outs[0][0]) and np.array_equal(a[1], outs[0][1])
+    d_o = np.abs(to_np_f64(o1) - to_np_f64(o2))[:, :, :380].max()
+    d_l = np.abs(to_np_f64(l1) - to_np_f64(l2))[:, :, :380].max()
+    print(f"[balanced vs per-qtile kv={kv_valid}] O {d_o:.2e} LSE {d_l:.2e}", flush=True)
+    assert d_o < 4e-3 and d_l < 1e-4
+    og2, lg2 = to_np_f64(o2), to_np_f64(l2)
+    O_r, L_r = oracle.attention(oracle.bf16_to_f64(q), oracle.bf16_to_f64(k), oracle.bf16_to_f64(v), 380, kv_valid)
+    compare(og2, lg2, O_r, L_r, valid, f"balanced kv={kv_valid}")
+    assert_pad_rows(og2, lg2, valid, "balanced")
