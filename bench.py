@@ -7,11 +7,19 @@ One step = one pass of the whole path over one batch of synthetic tokens:
 Inputs are resident in HBM before timing starts. Throughput is counted over
 valid tokens: FLOP = 4 * B * H * S_valid^2 * d per step.
 
-Prints ONE JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+Prints ONE JSON line:
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-configs]
+
+Counter collection (HBM traffic of the attention kernel, calibrated against a
+plain copy of known size), run under rocprofv3 once per counter:
+  python bench.py --pmc-target              # launches only the measured kernels
+  python bench.py --traffic-summary FETCH_DIR WRITE_DIR   # writes the profiles/ record
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +31,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (MI355X published dense peak)
 PEAK_HBM_GBS = 8000.0
 METRIC = "attn fwd TFLOP/s at Wan S=4736,H=10,d=128 bf16; % of bf16 MFMA peak"
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_wan480_traffic.json")
+COPY_CAL_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
+KERNEL_SOURCES = ("long_sequence_attention_amd/csrc/attn_fwd.hip", "long_sequence_attention_amd/csrc/common.h")
 
 
 def parse():
@@ -32,26 +43,194 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan480")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config kernel table")
     ap.add_argument("--kernel-iters", type=int, default=50)
+    ap.add_argument("--pmc-target", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- helpers
+def dev_tensors(w, np, torch, dev):
+    import workloads as W
+    q, k, v = W.make_qkv(w)
+    tod = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    return (q, k, v), (tod(q), tod(k), tod(v))
+
+
+def time_us(torch, fn, n, warm=3):
+    """Average microseconds per call of fn over n back-to-back calls, HIP
+    events on torch's current stream (the stream every dit_* call uses)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n * 1e3
 
 
 def cpu_baseline(w, q, k, v):
     """The fp64 oracle as it stands, timed on this host over the whole
-    workload (all heads, all rows: ~10 s on 8 cores)."""
+    workload (all heads, all valid rows), best of three runs."""
     import oracle
+    import workloads as W
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    pos = __import__("workloads").positions(w)
-    t0 = time.perf_counter()
-    oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
-    dt = time.perf_counter() - t0
+    pos = W.positions(w)
+    walls = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
+        walls.append(time.perf_counter() - t0)
+    dt = min(walls)
     return {"value": w.valid_flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full {w.name} workload (B={w.B}, H={w.H}, all {w.s_valid} valid query rows), "
-                      f"NumPy float64, {dt:.2f} s wall"}
+            "sample": f"full {w.name} workload (B={w.B}, H={w.H}, all {w.s_valid} valid query rows, RoPE tables, "
+                      f"RoPE, attention, LSE), NumPy float64, best of 3: {dt:.2f} s wall"}
+
+
+def read_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter
+    record, or None when the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter record"
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return rec["hbm_bytes_per_launch"], rec.get("command", "")
+
+
+# ------------------------------------------------------- counter workflow
+def pmc_target(args):
+    """Launch the dominant kernel (attention with K already rotated) and the
+    calibration copy a few times each; nothing else runs on the GPU."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import long_sequence_attention_amd as ops
+    ops.library_path()
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    _, (qd, kd, vd) = dev_tensors(w, np, torch, dev)
+    cos, sin = ops.rope_split_tables(torch.from_numpy(W.positions(w)).to(dev), w.axes, w.d, w.theta)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev)
+    for _ in range(5):
+        ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=(cos, sin), rope_k=None, out=o, lse=lse)
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    rows = COPY_CAL_BYTES // 4096
+    for _ in range(5):  # a plain copy: pad with s_pad == s_valid
+        ops.pad_tokens(src.view(1, rows, 4096), rows, out=dst.view(1, rows, 4096))
+    torch.cuda.synchronize()
+    print("pmc target done", flush=True)
+
+
+def traffic_summary(args):
+    import csv
+
+    def per_dispatch(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                kind = "attn" if "attn_fwd_kernel" in r["Kernel_Name"] else (
+                    "copy" if "row_copy_kernel" in r["Kernel_Name"] else None)
+                if kind is None:
+                    continue
+                key = (kind, r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        out = {}
+        for (kind, _), v in vals.items():
+            out.setdefault(kind, []).append(v)
+        return {k: sorted(v)[len(v) // 2] for k, v in out.items()}  # median over dispatches, KiB
+
+    fetch = per_dispatch(args.traffic_summary[0], "FETCH_SIZE")
+    write = per_dispatch(args.traffic_summary[1], "WRITE_SIZE")
+    f_fac = COPY_CAL_BYTES / (fetch["copy"] * 1024.0)
+    w_fac = COPY_CAL_BYTES / (write["copy"] * 1024.0)
+    rec = {
+        "kernel": "attn_fwd_kernel<128, false> (wan480, K pre-rotated)",
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "fetch_kib_per_launch_raw": fetch["attn"], "write_kib_per_launch_raw": write["attn"],
+        "copy_fetch_kib_raw": fetch["copy"], "copy_write_kib_raw": write["copy"],
+        "copy_bytes_each_way": COPY_CAL_BYTES,
+        "fetch_scale": f_fac, "write_scale": w_fac,
+        "hbm_fetch_bytes_per_launch": fetch["attn"] * 1024.0 * f_fac,
+        "hbm_write_bytes_per_launch": write["attn"] * 1024.0 * w_fac,
+        "hbm_bytes_per_launch": fetch["attn"] * 1024.0 * f_fac + write["attn"] * 1024.0 * w_fac,
+        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py --pmc-target",
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+# -------------------------------------------------------------- the bench
+def config_table(np, torch, ops, W, dev, n_iter):
+    """Attention throughput on every config (dit_attn_fwd call = K rotation
+    pre-pass + fused kernel; the Wan 720p config also as 4 key shards plus
+    dit_lse_merge)."""
+    res = {}
+    for name in ("tiny", "flux", "wan480", "hunyuan", "wan720"):
+        w = W.WORKLOADS[name]
+        _, (qd, kd, vd) = dev_tensors(w, np, torch, dev)
+        cos, sin = ops.rope_split_tables(torch.from_numpy(W.positions(w)).to(dev), w.axes, w.d, w.theta)
+        o = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid,
+                                                     rope_q=(cos, sin), rope_k=(cos, sin)), 256),
+                         dtype=torch.uint8, device=dev)
+        n = max(3, n_iter if w.valid_flop < 1e12 else 3)
+        us = time_us(torch, lambda: ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid,
+                                                 rope_q=(cos, sin), rope_k=(cos, sin), out=o, lse=lse,
+                                                 workspace=ws), n)
+        ent = {"us": us, "tflops": w.valid_flop / us / 1e6, "pct_peak": w.valid_flop / us / 1e6 / PEAK_BF16_TFLOPS * 100}
+        if w.n_key_shards > 1:
+            shards = W.key_shards(w)
+            po = [torch.empty((w.B, w.H, w.s_pad, w.d), dtype=torch.float32, device=dev) for _ in shards]
+            pl = [torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev) for _ in shards]
+            tabs = [(cos[s0:s0 + L].contiguous(), sin[s0:s0 + L].contiguous()) for (s0, L, _) in shards]
+            wss = [torch.empty(max(ops.attn_workspace_size(qd, kd[:, :, s0:s0 + L], vd[:, :, s0:s0 + L],
+                                                           kv_valid=kvv, rope_q=(cos, sin), rope_k=tabs[i]), 256),
+                               dtype=torch.uint8, device=dev) for i, (s0, L, kvv) in enumerate(shards)]
+            om = torch.empty_like(qd)
+
+            def sharded():
+                for i, (s0, L, kvv) in enumerate(shards):
+                    ops.attn_fwd(qd, kd[:, :, s0:s0 + L], vd[:, :, s0:s0 + L], q_valid=w.s_valid, kv_valid=kvv,
+                                 rope_q=(cos, sin), rope_k=tabs[i], out=po[i], lse=pl[i], workspace=wss[i])
+                ops.lse_merge(po, pl, q_valid=w.s_valid, out=om, lse_out=lse)
+
+            us_m = time_us(torch, lambda: ops.lse_merge(po, pl, q_valid=w.s_valid, out=om, lse_out=lse), 10)
+            us_s = time_us(torch, sharded, 3, warm=1)
+            merge_bytes = len(shards) * (w.B * w.H * w.s_pad * (w.d * 4 + 4)) + w.B * w.H * w.s_pad * (w.d * 2 + 4)
+            ent.update({"sharded_4_plus_merge_us": us_s, "sharded_tflops": w.valid_flop / us_s / 1e6,
+                        "lse_merge_us": us_m, "lse_merge_GBps": merge_bytes / us_m / 1e3})
+            del po, pl, wss, om
+        res[name] = ent
+        del qd, kd, vd, o, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -60,6 +239,13 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                           "(the path shards by head across GPUs; see DESIGN.md)"}))
         sys.exit(2)
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
+    if args.pmc_target:
+        pmc_target(args)
+        return
+    import ctypes
     import numpy as np
     import torch
     import workloads as W
@@ -70,7 +256,8 @@ def main():
     dev = torch.device("cuda:0")
     B, H, d, Sv, Sp = w.B, w.H, w.d, w.s_valid, w.s_pad
 
-    q, k, v = W.make_qkv(w)
+    (q, k, v), _ = dev_tensors(w, np, torch, torch.device("cpu"))
+
     # token-major inputs [B, S_valid, H, d] (what an all-to-all hands over)
     def tok(x):
         t = torch.from_numpy(np.ascontiguousarray(x[:, :, :Sv].transpose(0, 2, 1, 3)).view(np.int16))
@@ -84,9 +271,7 @@ def main():
     cos = torch.empty((Sp, d // 2), dtype=torch.float32, device=dev)
     sin = torch.empty_like(cos)
     L = ops._native.lib()
-    import ctypes
     chans = (ctypes.c_int32 * len(w.axes))(*w.axes)
-
     qv, kv_, vv = qp.transpose(1, 2), kp.transpose(1, 2), vp.transpose(1, 2)
     ws = torch.empty(ops.attn_workspace_size(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin)),
                      dtype=torch.uint8, device=dev)
@@ -99,15 +284,14 @@ def main():
         ops.pad_tokens(q_tok, Sp, out=qp)
         ops.pad_tokens(k_tok, Sp, out=kp)
         ops.pad_tokens(v_tok, Sp, out=vp)
-        ops.attn_fwd(qp.transpose(1, 2), kp.transpose(1, 2), vp.transpose(1, 2), q_valid=Sv, kv_valid=Sv,
-                     rope_q=(cos, sin), rope_k=(cos, sin), out=op.transpose(1, 2), lse=lse, workspace=ws)
+        ops.attn_fwd(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin),
+                     out=op.transpose(1, 2), lse=lse, workspace=ws)
         ops.unpad_tokens(op, Sv, out=o_tok)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
         step()
@@ -115,40 +299,28 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # Dominant kernel alone: one attention-kernel launch per call (K already
-    # rotated, so dit_attn_fwd launches only the fused attention kernel).
-    k_rot = torch.empty((B, H, Sp, d), dtype=torch.bfloat16, device=dev)
-    ops.attn_fwd(qp.transpose(1, 2), kp.transpose(1, 2), vp.transpose(1, 2), q_valid=Sv, kv_valid=Sv,
-                 rope_q=(cos, sin), rope_k=(cos, sin), out=op.transpose(1, 2), lse=lse, workspace=ws)
-    torch.cuda.synchronize()
-    k_rot.view(-1).copy_(ws[: B * H * Sp * d * 2].view(torch.bfloat16)[: B * H * Sp * d])
+    # Dominant kernel alone: with K already rotated, dit_attn_fwd launches
+    # exactly one kernel (the fused attention kernel) per call.
+    k_rot = ws[: B * H * Sp * d * 2].view(torch.bfloat16).view(B, H, Sp, d).clone()
 
     def attn_only():
-        ops.attn_fwd(qp.transpose(1, 2), k_rot, vp.transpose(1, 2), q_valid=Sv, kv_valid=Sv,
-                     rope_q=(cos, sin), rope_k=None, out=op.transpose(1, 2), lse=lse)
-
-    def time_loop(fn, n):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(n):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n * 1e3  # us
+        ops.attn_fwd(qv, k_rot, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=None,
+                     out=op.transpose(1, 2), lse=lse)
 
     n = args.kernel_iters
-    us_attn = time_loop(attn_only, n)
-    us_pad = time_loop(lambda: ops.pad_tokens(q_tok, Sp, out=qp), n)
-    us_unpad = time_loop(lambda: ops.unpad_tokens(op, Sv, out=o_tok), n)
-    us_attn_call = time_loop(lambda: ops.attn_fwd(qp.transpose(1, 2), kp.transpose(1, 2), vp.transpose(1, 2),
-                                                  q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin),
-                                                  out=op.transpose(1, 2), lse=lse, workspace=ws), n)
+    us_attn = time_us(torch, attn_only, n)
+    us_tables = time_us(torch, lambda: ops._native.check(L.dit_rope_split_tables(
+        ctypes.c_void_p(pos.data_ptr()), Sp, len(w.axes), chans, d, float(w.theta), ctypes.c_void_p(cos.data_ptr()),
+        ctypes.c_void_p(sin.data_ptr()), ops._stream(dev)), "tables"), n)
+    us_pad = time_us(torch, lambda: ops.pad_tokens(q_tok, Sp, out=qp), n)
+    us_unpad = time_us(torch, lambda: ops.unpad_tokens(op, Sv, out=o_tok), n)
+    us_call = time_us(torch, lambda: ops.attn_fwd(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin),
+                                                  rope_k=(cos, sin), out=op.transpose(1, 2), lse=lse,
+                                                  workspace=ws), n)
     flop = w.valid_flop
     achieved = flop / (us_attn * 1e-6) / 1e12
     pad_bytes = (Sv + Sp) * H * d * 2 * B
+    traffic, traffic_src = read_traffic()
 
     out = {
         "metric": METRIC,
@@ -164,15 +336,22 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "B": B, "H": H, "d": d, "s_valid": Sv, "s_pad": Sp,
-                   "flop_per_step": flop, "step": "tables + pad(Q,K,V) + attn_fwd(K-rope pre-pass + fused kernel) + unpad(O)"},
+                   "flop_per_step": flop,
+                   "step": "tables + pad(Q,K,V) + attn_fwd(K-rope pre-pass + fused kernel) + unpad(O)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "attn_fwd_kernel<128>", "kernel_us": us_attn},
-        "kernels_us": {"attn_fwd_kernel": us_attn, "dit_attn_fwd_call(prepass+kernel)": us_attn_call,
-                       "pad_tokens(one tensor)": us_pad, "unpad_tokens": us_unpad,
-                       "pad_GBps": pad_bytes / (us_pad * 1e-6) / 1e9},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch", "traffic_source": traffic_src,
+                     "algorithmic_flop_per_launch": flop, "kernel": "attn_fwd_kernel<128, false>",
+                     "kernel_us": us_attn},
+        "kernels_us": {"attn_fwd_kernel": us_attn, "dit_attn_fwd_call(K pre-pass + kernel)": us_call,
+                       "rope_tables": us_tables, "pad_tokens(one tensor)": us_pad, "unpad_tokens": us_unpad,
+                       "pad_GBps": pad_bytes / (us_pad * 1e-6) / 1e9,
+                       "unpad_GBps": 2 * Sv * H * d * 2 * B / (us_unpad * 1e-6) / 1e9},
         "pct_of_peak_step": flop / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS * 100,
     }
+    del k_rot
+    if not args.no_configs:
+        out["configs_attn_fwd"] = config_table(np, torch, ops, W, dev, n)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(out), flush=True)

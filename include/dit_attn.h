@@ -152,7 +152,8 @@ DIT_API int dit_lse_merge(int n_parts, const void *const *o_parts, const float *
  *   cos_out[s, P_a + j] = cos(pos[s, a] * theta^(-2j/c_a)), sin_out likewise.
  * Angles and sines are evaluated in fp64 and rounded to fp32. Position 0 is
  * the identity rotation (text tokens, pad rows). cos_out/sin_out: device fp32
- * [S, d/2]. 1 <= n_axes <= 8, 2 <= d <= 256.
+ * [S, d/2]. 1 <= n_axes <= 8, 2 <= d <= 256 (else DIT_ERR_INVALID);
+ * S * d/2 >= 2^31 gives DIT_ERR_UNSUPPORTED.
  */
 DIT_API int dit_rope_split_tables(const int32_t *pos, int S, int n_axes, const int32_t *axis_channels,
                           int d, float theta, float *cos_out, float *sin_out, void *stream);
@@ -160,12 +161,16 @@ DIT_API int dit_rope_split_tables(const int32_t *pos, int S, int n_axes, const i
 /*
  * Tail padding of token rows: in [B, s_valid, row_bytes] -> out
  * [B, s_pad, row_bytes], rows >= s_valid of `out` set to zero bytes
- * (Difflet PR #153 Wan padding commit, 4680 -> 4736).
+ * (Difflet PR #153 Wan padding commit, 4680 -> 4736). Both buffers are
+ * dense device memory owned by the caller; they must not alias.
+ * DIT_ERR_INVALID: B < 1, s_valid < 0, s_pad < s_valid, row_bytes <= 0, a
+ * required NULL pointer, in == out. DIT_ERR_UNSUPPORTED: B > 65535.
  */
 DIT_API int dit_pad_tokens(const void *in, void *out, int B, int s_valid, int s_pad,
                    int64_t row_bytes, void *stream);
 
-/* Inverse of dit_pad_tokens: in [B, s_pad, row_bytes] -> out [B, s_valid, row_bytes]. */
+/* Inverse of dit_pad_tokens: in [B, s_pad, row_bytes] -> out [B, s_valid, row_bytes]
+ * (no in-place operation; same status codes as dit_pad_tokens). */
 DIT_API int dit_unpad_tokens(const void *in, void *out, int B, int s_pad, int s_valid,
                      int64_t row_bytes, void *stream);
 

@@ -78,6 +78,8 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   if (!std::isfinite(scale) || scale < 0.0f) return fail(DIT_ERR_INVALID, "sm_scale=%g must be finite and positive", (double)d->sm_scale);
   const int64_t nq = ((int64_t)d->s_q + 127) / 128;
   if (nq * d->H * d->B > 0x7fffffffLL) return fail(DIT_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  if (d->cos_k != nullptr && (d->H > 65535 || d->B > 65535))
+    return fail(DIT_ERR_UNSUPPORTED, "K rotation needs B, H <= 65535 (one grid plane per head)");
   const void *ptrs[] = {d->q, d->k, d->v, d->o, d->cos_q, d->sin_q, d->cos_k, d->sin_k};
   for (const void *p : ptrs)
     if (p != nullptr && !aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
@@ -302,6 +304,7 @@ int dit_rope_split_tables(const int32_t *pos, int S, int n_axes, const int32_t *
   if (axis_channels == nullptr) return fail(DIT_ERR_INVALID, "axis_channels is NULL");
   if (d < 2 || d > 2 * dit::kMaxPairs || d % 2) return fail(DIT_ERR_INVALID, "d=%d must be even and in [2, %d]", d, 2 * dit::kMaxPairs);
   if (!(theta > 0.0f) || !std::isfinite(theta)) return fail(DIT_ERR_INVALID, "theta must be finite and positive");
+  if ((int64_t)S * (d / 2) > 0x7fffffffLL) return fail(DIT_ERR_UNSUPPORTED, "S * d/2 must be below 2^31");
   int sum = 0;
   for (int a = 0; a < n_axes; ++a) {
     if (axis_channels[a] <= 0 || axis_channels[a] % 2)
@@ -336,6 +339,7 @@ int dit_pad_tokens(const void *in, void *out, int B, int s_valid, int s_pad, int
   if (s_pad > 0 && out == nullptr) return fail(DIT_ERR_INVALID, "out is NULL");
   if (s_valid > 0 && in == nullptr) return fail(DIT_ERR_INVALID, "in is NULL");
   if (in != nullptr && in == out) return fail(DIT_ERR_INVALID, "in and out must not alias");
+  if (B > 65535) return fail(DIT_ERR_UNSUPPORTED, "B > 65535 (one grid row per batch)");
   return hip_status(dit::launch_row_copy(in, out, B, s_valid, s_pad, s_valid, row_bytes, reinterpret_cast<hipStream_t>(stream)),
                     "pad launch");
 }
@@ -345,6 +349,7 @@ int dit_unpad_tokens(const void *in, void *out, int B, int s_pad, int s_valid, i
     return fail(DIT_ERR_INVALID, "need B >= 1, 0 <= s_valid <= s_pad, row_bytes > 0");
   if (s_valid > 0 && (out == nullptr || in == nullptr)) return fail(DIT_ERR_INVALID, "in and out must be non-NULL");
   if (in != nullptr && in == out) return fail(DIT_ERR_INVALID, "in and out must not alias (no in-place unpad)");
+  if (B > 65535) return fail(DIT_ERR_UNSUPPORTED, "B > 65535 (one grid row per batch)");
   return hip_status(dit::launch_row_copy(in, out, B, s_pad, s_valid, s_valid, row_bytes, reinterpret_cast<hipStream_t>(stream)),
                     "unpad launch");
 }

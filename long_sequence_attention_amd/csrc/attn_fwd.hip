@@ -647,34 +647,28 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   }
 }
 
+// K rotation pre-pass: head (blockIdx.y, blockIdx.z) rows s < valid, one
+// thread per 8-channel run of the first half and its partner run d/2 later.
+// RUNS = d/16 threads per row, 256/RUNS rows per block iteration.
+template <int RUNS>
 __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
-  const int runs = p.d / 16;
-  const int half = p.d / 2;
-  const int64_t total = (int64_t)p.B * p.H * p.valid * runs;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int c = (int)(t % runs);
-    int64_t r = t / runs;
-    const int s = (int)(r % p.valid);
-    r /= p.valid;
-    const int h = (int)(r % p.H);
-    const int b = (int)(r / p.H);
-    const bf16_t *xr = p.x + b * p.xs_b + h * p.xs_h + (int64_t)s * p.xs_s;
-    bf16_t *yr = p.y + (((int64_t)b * p.H + h) * p.S + s) * p.d;
+  constexpr int ROWS = 256 / RUNS, HALF = RUNS * 8;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int c = threadIdx.x % RUNS;
+  const bf16_t *xh = p.x + b * p.xs_b + h * p.xs_h;
+  bf16_t *yh = p.y + ((int64_t)b * p.H + h) * p.S * (2 * HALF);
+  for (int s = blockIdx.x * ROWS + threadIdx.x / RUNS; s < p.valid; s += gridDim.x * ROWS) {
+    const bf16_t *xr = xh + (int64_t)s * p.xs_s;
+    bf16_t *yr = yh + (int64_t)s * (2 * HALF);
     u32x4 lo = ldg16(xr + c * 8);
-    u32x4 hi = ldg16(xr + half + c * 8);
-    const int64_t to = (int64_t)s * half + c * 8;
+    u32x4 hi = ldg16(xr + HALF + c * 8);
+    const int64_t to = (int64_t)s * HALF + c * 8;
     rotate8(lo, hi, p.cos_t + to, p.sin_t + to);
     *reinterpret_cast<u32x4 *>(yr + c * 8) = lo;
-    *reinterpret_cast<u32x4 *>(yr + half + c * 8) = hi;
+    *reinterpret_cast<u32x4 *>(yr + HALF + c * 8) = hi;
   }
 }
 
-// Balanced-schedule plan: workgroup w owns units [begin(w), begin(w+1)) of
-// the (q-tile, key-tile) space, q-tile major, with begin(w) = w*units/groups.
-// Writes each workgroup's (at most two) runs, each q-tile's owner range,
-// partial slots (2w for a workgroup's first run, 2w+1 for its last), and
-// zeroes the arrival counters.
 __global__ __launch_bounds__(256) void sk_plan_kernel(int4 *table, int2 *owners, int32_t *count, int groups,
                                                       int n_qt, int nk) {
   const int64_t units = (int64_t)n_qt * nk;
@@ -726,11 +720,16 @@ hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream) {
 }
 
 hipError_t launch_rope_rotate(const RopeRotateParams &p, hipStream_t stream) {
-  const int64_t total = (int64_t)p.B * p.H * p.valid * (p.d / 16);
-  if (total <= 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(rope_rotate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  if ((int64_t)p.B * p.H * p.valid <= 0) return hipSuccess;
+  const int runs = p.d / 16;
+  const int rows = 256 / runs;
+  int bx = (p.valid + rows - 1) / rows;
+  // about 2048 blocks in all, each striding over its head's rows
+  const int cap = (int)((2048 + (int64_t)p.B * p.H - 1) / ((int64_t)p.B * p.H));
+  if (bx > cap) bx = cap < 1 ? 1 : cap;
+  const dim3 grid((unsigned)bx, (unsigned)p.H, (unsigned)p.B);
+  if (runs == 8) hipLaunchKernelGGL(rope_rotate_kernel<8>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(rope_rotate_kernel<4>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -15,12 +15,12 @@ namespace {
 
 // One thread per table entry (s, pair j): angle = pos[s, axis(j)] * freq[j]
 // evaluated in fp64, cos/sin in fp64, rounded once to fp32.
+// (S * d/2 < 2^31 is checked by the caller, so the index math is 32-bit.)
 __global__ __launch_bounds__(256) void rope_tables_kernel(TableParams p) {
-  const int64_t total = (int64_t)p.S * p.half_d;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int s = (int)(t / p.half_d);
-    const int j = (int)(t % p.half_d);
+  const int total = p.S * p.half_d;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < total; t += gridDim.x * blockDim.x) {
+    const int s = t / p.half_d;
+    const int j = t - s * p.half_d;
     const double ang = (double)p.pos[(int64_t)s * p.n_axes + p.axis[j]] * p.freq[j];
     double sn, cs;
     sincos(ang, &sn, &cs);
@@ -29,21 +29,31 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(TableParams p) {
   }
 }
 
-// out row s of batch b = in row s for s < n_copy, else zero. V is the copy
-// granule (16, 4 or 1 bytes), chosen from the row size and alignment.
-template <typename V>
+// Tail pad / unpad of one batch (blockIdx.y): rows 0..n_copy-1 of both
+// sides are one contiguous run, so out[i] = in[i] for i < n_copy granules
+// and out[i] = 0 up to n_total. V is the copy granule (16, 4 or 1 bytes),
+// chosen from the row size and alignment. Each thread keeps UNROLL granules
+// in flight, a grid stride apart, so consecutive lanes stay on consecutive
+// addresses.
+template <typename V, int UNROLL>
 __global__ __launch_bounds__(256) void row_copy_kernel(const V *__restrict__ in, V *__restrict__ out,
-                                                      int s_in, int s_out, int n_copy,
-                                                      int64_t row_vec, int64_t total) {
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = t / row_vec;
-    const int64_t v = t - r * row_vec;
-    const int64_t b = r / s_out;
-    const int64_t s = r - b * s_out;
-    V val{};
-    if (s < n_copy) val = in[(b * s_in + s) * row_vec + v];
-    out[t] = val;
+                                                      int64_t in_batch, int64_t out_batch, int64_t n_copy,
+                                                      int64_t n_total) {
+  const V *src = in + (int64_t)blockIdx.y * in_batch;
+  V *dst = out + (int64_t)blockIdx.y * out_batch;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n_total; i0 += stride * UNROLL) {
+    V v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t i = i0 + u * stride;
+      v[u] = (i < n_copy) ? src[i] : V{};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n_total) dst[i] = v[u];
+    }
   }
 }
 
@@ -113,23 +123,26 @@ hipError_t launch_rope_tables(const TableParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename V>
+static void launch_copy_v(const void *in, void *out, int B, int s_in, int s_out, int n_copy, int64_t row_bytes,
+                          hipStream_t stream) {
+  constexpr int UNROLL = 4;
+  const int64_t rv = row_bytes / (int64_t)sizeof(V);
+  const int64_t n_total = (int64_t)s_out * rv;
+  int64_t blocks = (n_total + 256 * UNROLL - 1) / (256 * UNROLL);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL((row_copy_kernel<V, UNROLL>), dim3((unsigned)blocks, (unsigned)B), dim3(256), 0, stream,
+                     static_cast<const V *>(in), static_cast<V *>(out), (int64_t)s_in * rv, n_total,
+                     (int64_t)n_copy * rv, n_total);
+}
+
 hipError_t launch_row_copy(const void *in, void *out, int B, int s_in, int s_out, int n_copy,
                            int64_t row_bytes, hipStream_t stream) {
   if ((int64_t)B * s_out * row_bytes == 0) return hipSuccess;
   const uintptr_t a = reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out);
-  if (row_bytes % 16 == 0 && a % 16 == 0) {
-    const int64_t rv = row_bytes / 16, total = (int64_t)B * s_out * rv;
-    hipLaunchKernelGGL(row_copy_kernel<uint4>, dim3(grid_for(total)), dim3(256), 0, stream,
-                       (const uint4 *)in, (uint4 *)out, s_in, s_out, n_copy, rv, total);
-  } else if (row_bytes % 4 == 0 && a % 4 == 0) {
-    const int64_t rv = row_bytes / 4, total = (int64_t)B * s_out * rv;
-    hipLaunchKernelGGL(row_copy_kernel<uint32_t>, dim3(grid_for(total)), dim3(256), 0, stream,
-                       (const uint32_t *)in, (uint32_t *)out, s_in, s_out, n_copy, rv, total);
-  } else {
-    const int64_t rv = row_bytes, total = (int64_t)B * s_out * rv;
-    hipLaunchKernelGGL(row_copy_kernel<uint8_t>, dim3(grid_for(total)), dim3(256), 0, stream,
-                       (const uint8_t *)in, (uint8_t *)out, s_in, s_out, n_copy, rv, total);
-  }
+  if (row_bytes % 16 == 0 && a % 16 == 0) launch_copy_v<uint4>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
+  else if (row_bytes % 4 == 0 && a % 4 == 0) launch_copy_v<uint32_t>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
+  else launch_copy_v<uint8_t>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
   return hipGetLastError();
 }
 
