@@ -76,7 +76,7 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   float scale = d->sm_scale;
   if (scale == 0.0f) scale = 1.0f / std::sqrt((float)d->d);
   if (!std::isfinite(scale) || scale < 0.0f) return fail(DIT_ERR_INVALID, "sm_scale=%g must be finite and positive", (double)d->sm_scale);
-  const int64_t nq = ((int64_t)d->s_q + 127) / 128;
+  const int64_t nq = ((int64_t)d->s_q + dit::kAttnBlockM - 1) / dit::kAttnBlockM;
   if (nq * d->H * d->B > 0x7fffffffLL) return fail(DIT_ERR_UNSUPPORTED, "too many query tiles for one launch");
   if (d->cos_k != nullptr && (d->H > 65535 || d->B > 65535))
     return fail(DIT_ERR_UNSUPPORTED, "K rotation needs B, H <= 65535 (one grid plane per head)");
@@ -114,7 +114,7 @@ struct AttnPlan {
   size_t total = 0;
 };
 
-constexpr int kBlockM = 128, kBlockN = 64, kThreads = 256;
+constexpr int kBlockM = dit::kAttnBlockM, kBlockN = dit::kAttnBlockN, kThreads = dit::kAttnThreads;
 
 int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   AttnPlan p;
@@ -133,7 +133,7 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       return fail(DIT_ERR_HIP, "cannot query the compute-unit count of the current device");
-    const int64_t slots = 2LL * cus;   // two 4-wave workgroups fit one CU
+    const int64_t slots = (int64_t)(512 / dit::kAttnThreads) * cus;   // workgroups resident per CU (two waves per SIMD)
     // whole rounds of slots, and at least as many workgroups as q-tiles so
     // a workgroup's run of key tiles spans at most two q-tiles
     int64_t g = slots * ((nq + slots - 1) / slots);
@@ -223,7 +223,7 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
   p.B = d.B; p.H = d.H; p.s_q = d.s_q; p.s_kv = d.s_kv;
   p.q_valid = d.q_valid; p.kv_valid = d.kv_valid;
   p.o_f32 = d.o_dtype == DIT_F32;
-  p.n_qtiles = (d.s_q + 127) / 128;
+  p.n_qtiles = (d.s_q + dit::kAttnBlockM - 1) / dit::kAttnBlockM;
   p.scale_log2 = scale * 1.4426950408889634f;
 
   if (pl.k_bytes > 0) {

@@ -9,7 +9,7 @@
 // PR #376 for the natural-log LSE returned beside O; maxdiffusion PR #491 for
 // masking pads through the real KV length).
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+// Work decomposition (one workgroup = 8 waves = 256 query rows of one head):
 //   * Each wave owns 32 query rows and computes S^T = K Q^T, so a lane holds
 //     16 scores of ONE query (lane % 32) per 32-key block: the row max is an
 //     in-register reduction plus one v_permlane32_swap with lane ^ 32.
@@ -47,9 +47,9 @@ namespace dit {
 
 namespace {
 
-constexpr int BM = 128;   // query rows per workgroup
-constexpr int BN = 64;    // keys per tile
-constexpr int NT = 256;   // threads per workgroup
+constexpr int BM = kAttnBlockM;   // query rows per workgroup
+constexpr int BN = kAttnBlockN;   // keys per tile
+constexpr int NT = kAttnThreads;   // threads per workgroup
 constexpr float kLazyRescale = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -94,7 +94,7 @@ struct Geo {
   static constexpr int CPR = D / 8;
   static constexpr int RPB = 16 / CPR;
   static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / 4;
+  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / kAttnWaves;
   static constexpr int K0 = 0, V0 = 2 * TILE_BYTES;
   __device__ static constexpr int fk(int r) { return (r / RPB) % CPR; }
   __device__ static constexpr int fv(int r) { return 4 * ((r / RPB) % (4 / RPB)); }
@@ -548,7 +548,7 @@ __device__ __forceinline__ kernarg_params_t &kernarg_params() {
 }
 
 template <int D, bool BALANCED>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   using G = Geo<D>;
   constexpr int DK = D / 16;
   constexpr int DB = D / 32;

@@ -26,6 +26,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// Attention tiling shared by the kernels and the host planning code: a
+// workgroup of kAttnWaves waves owns kAttnBlockM = 32 * kAttnWaves query
+// rows of one head and walks the keys in tiles of kAttnBlockN rows.
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnBlockM = 32 * kAttnWaves;
+constexpr int kAttnBlockN = 64;
+
 // Parameters of the attention forward kernel (passed by value).
 struct AttnParams {
   const bf16_t *q, *k, *v;
@@ -43,8 +51,8 @@ struct AttnParams {
   // balanced schedule (sk_groups > 0): workgroup w owns a contiguous run of
   // (q-tile, key-tile) units; split q-tiles meet in the workspace below
   int32_t sk_groups;
-  float *sk_part_o;  // [2 * sk_groups][256 threads][d/2] partial O / l, fp32
-  float *sk_part_l;  // [2 * sk_groups][128 rows] partial LSE, log2 units
+  float *sk_part_o;  // [2 * sk_groups][kAttnThreads][d/2] partial O / l, fp32
+  float *sk_part_l;  // [2 * sk_groups][kAttnBlockM rows] partial LSE, log2 units
   int32_t *sk_count; // [B * H * n_qtiles] arrival counters, zero on entry
   const int4 *sk_table;  // [2 * sk_groups] runs {q-tile, kb, ke, slot or -1}
   const int2 *sk_owners; // [B * H * n_qtiles] first and last workgroup of each q-tile
