@@ -39,12 +39,13 @@ KERNEL_SOURCES = ("long_sequence_attention_amd/csrc/attn_fwd.hip", "long_sequenc
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the clocks settle only after a few hundred ms of sustained load
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="wan480")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config kernel table")
-    ap.add_argument("--kernel-iters", type=int, default=50)
+    ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return ap.parse_args()
@@ -66,12 +67,18 @@ def dev_tensors(w, np, torch, dev):
     return (q, k, v), (tod(q), tod(k), tod(v))
 
 
-def time_us(torch, fn, n, warm=3):
+def time_us(torch, fn, n, warm=3, warm_s=0.0):
     """Average microseconds per call of fn over n back-to-back calls, HIP
-    events on torch's current stream (the stream every dit_* call uses)."""
+    events on torch's current stream (the stream every dit_* call uses),
+    after `warm` calls and at least warm_s seconds of calls."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_s
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(n):
@@ -308,7 +315,7 @@ def main():
                      out=op.transpose(1, 2), lse=lse)
 
     n = args.kernel_iters
-    us_attn = time_us(torch, attn_only, n)
+    us_attn = time_us(torch, attn_only, n, warm_s=1.0)
     us_tables = time_us(torch, lambda: ops._native.check(L.dit_rope_split_tables(
         ctypes.c_void_p(pos.data_ptr()), Sp, len(w.axes), chans, d, float(w.theta), ctypes.c_void_p(cos.data_ptr()),
         ctypes.c_void_p(sin.data_ptr()), ops._stream(dev)), "tables"), n)

@@ -27,11 +27,12 @@
 //     (MFMA row m = 16a+8b+4c+j holds key 16a+8c+4b+j) so the scores a lane
 //     gets back from the S^T MFMA are exactly the 8-key runs it feeds as the
 //     P^T operand: P goes from accumulator to operand with one bf16 pack.
-//   * Software pipeline: K runs one tile ahead of V. While the softmax of
-//     tile t runs on the VALU, the S MFMAs of tile t+1 run on the matrix
-//     cores (interleaved with sched_group_barrier); then P(t).V(t) runs while
-//     the row max of tile t+1 is taken. Two tiles per loop iteration keep
-//     the score registers and LDS buffer parity static.
+//   * Software pipeline: K runs one tile ahead of V. The softmax of tile t
+//     (VALU) is interleaved (sched_group_barrier) with the S MFMAs of tile
+//     t+1 and the P(t).V(t) MFMAs, split so both MFMA groups carry VALU
+//     work; the row max of tile t+1 is taken beside P(t).V(t). Two tiles
+//     per loop iteration keep the score registers and LDS buffer parity
+//     static.
 //   * exp2 with scale*log2(e) folded into one FMA, and a lazy rescale: the
 //     running max is only raised (and O, l rescaled) when a tile max exceeds
 //     it by more than 8 (log2 units), so p <= 2^8 stays exact in fp32/bf16
@@ -196,9 +197,11 @@ struct StepCtx {
   float c2;
 };
 
-// One key tile of the main loop. Block A: P(t) = exp2(S(t) - m) on VALU while
-// S(t+1) = K(t+1) Q^T runs on MFMA; block B: O^T += V(t)^T P(t)^T on MFMA
-// while the row max of S(t+1) is taken. Then the (rare) lazy rescale.
+// One key tile of the main loop: S(t+1) = K(t+1) Q^T and O^T += V(t)^T
+// P(t)^T on the matrix cores, with the VALU work spread over both MFMA
+// groups (3 VALU ops per S MFMA, 5 per P.V MFMA): P(t) = exp2(S(t) - m) for
+// key block 0 runs beside S(t+1), block 1 beside the P.V of block 0, and
+// the row max of S(t+1) beside the rest. Then the (rare) lazy rescale.
 // par is the LDS buffer parity of tile t within the current key range.
 // STEADY: tile t+1 exists and is full, parity static, scheduled with
 // sched_group_barrier. Otherwise has_next / mask_next are run-time flags
@@ -220,8 +223,7 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
   const float neg_m = -m_run;
   bf16x8 pop[2][2];
   float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+  auto softmax_block = [&](int blk) {
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       f32x8 pv;
@@ -234,11 +236,13 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
         ps1 += pv[e + 1];
       }
     }
-  }
+  };
+  softmax_block(0);
   if (HAS_NEXT) {
     qk_tile<D>(cx.smem + G::K0 + (par ^ 1) * G::TILE_BYTES, kx, cx.qop, snext);
     if (!STEADY && mask_next) mask_tail(snext, (t + 1) * BN, cx.kv_valid, cx.hf);
   }
+  softmax_block(1);
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
@@ -261,14 +265,14 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
     for (int i = 0; i < 2 * DK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 96 / (2 * DK), 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
   }
   l_run += ps0 + ps1;
