@@ -199,7 +199,7 @@ struct StepCtx {
 
 // One key tile of the main loop: S(t+1) = K(t+1) Q^T and O^T += V(t)^T
 // P(t)^T on the matrix cores, with the VALU work spread over both MFMA
-// groups (3 VALU ops per S MFMA, 5 per P.V MFMA): P(t) = exp2(S(t) - m) for
+// groups (3 VALU ops per S MFMA, 4 per P.V MFMA): P(t) = exp2(S(t) - m) for
 // key block 0 runs beside S(t+1), block 1 beside the P.V of block 0, and
 // the row max of S(t+1) beside the rest. Then the (rare) lazy rescale.
 // par is the LDS buffer parity of tile t within the current key range.
@@ -272,7 +272,7 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
     for (int i = 0; i < 4 * DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
   }
   l_run += ps0 + ps1;
