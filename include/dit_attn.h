@@ -57,11 +57,14 @@ typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
 
 /* How dit_attn_fwd spreads work over the GPU (results agree to rounding;
  * each schedule is bit-reproducible from call to call):
- * AUTO currently resolves to PER_QTILE (one workgroup per 128-row query
- * tile), which measures fastest on MI355X for the shapes tested.
- * BALANCED gives every workgroup an equal run of (query tile, key tile)
- * pairs; query tiles split between workgroups are combined in the
- * workspace by the last workgroup to finish (no waiting between them). */
+ * PER_QTILE runs one workgroup per 256-row query tile over all keys.
+ * BALANCED splits the key range of every query tile into 2..8 equal pieces
+ * (the count chosen from the device's compute-unit count to even out the
+ * last wave of workgroups); each piece writes fp32 partial results to the
+ * workspace and the last piece of a tile to finish merges them in a fixed
+ * order (no workgroup waits for another).
+ * AUTO resolves to PER_QTILE, which measures faster on MI355X for the
+ * Wan, FLUX and HunyuanVideo shapes. */
 typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED = 2 } dit_schedule;
 
 /*
@@ -120,8 +123,10 @@ typedef struct dit_attn_desc {
   int32_t schedule;              /* dit_schedule */
 } dit_attn_desc;
 
-/* Bytes of workspace dit_attn_fwd needs for `desc` on the current device
- * (0 when K is not rotated and the schedule needs no partial results). */
+/* Bytes of workspace dit_attn_fwd needs for `desc` (0 when K is not rotated
+ * and the schedule needs no partial results). Under BALANCED the size depends
+ * on the current device's compute-unit count (DIT_ERR_HIP if it cannot be
+ * queried). */
 DIT_API int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes);
 
 /* Attention forward with fused RoPE and exact pad-key masking; see above. */

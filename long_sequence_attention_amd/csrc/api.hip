@@ -108,53 +108,64 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
 // their scratch lives inside the caller's workspace.
 struct AttnPlan {
   size_t k_bytes = 0;       // rotated K, dense [B, H, s_kv, d] bf16
-  int groups = 0;           // balanced-schedule workgroups (0 = one per q-tile)
-  size_t part_o_off = 0, part_l_off = 0, count_off = 0, table_off = 0, owners_off = 0;
+  int splits = 1;           // key-split pieces per q-tile (1 = one workgroup per q-tile)
+  size_t part_o_off = 0, part_l_off = 0, count_off = 0;
   int64_t n_counts = 0;
   size_t total = 0;
 };
 
 constexpr int kBlockM = dit::kAttnBlockM, kBlockN = dit::kAttnBlockN, kThreads = dit::kAttnThreads;
 
+// Estimated run time, in key tiles of one workgroup, of nq q-tiles over nk
+// key tiles cut into S pieces each on `slots` resident workgroups: whole
+// rounds of slots times the longest piece, plus 5% for the partials and the
+// merge when S > 1.
+double split_cost(int64_t nq, int64_t nk, int64_t S, int64_t slots) {
+  const int64_t rounds = (nq * S + slots - 1) / slots;
+  const int64_t piece = (nk + S - 1) / S;
+  return (double)(rounds * piece) * (S > 1 ? 1.05 : 1.0);
+}
+
 int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   AttnPlan p;
   if (d->cos_k != nullptr && d->kv_valid > 0) p.k_bytes = round_up((size_t)d->B * d->H * (size_t)d->s_kv * d->d * 2, 256);
   const int64_t nq = (int64_t)d->B * d->H * ((d->s_q + kBlockM - 1) / kBlockM);
   const int64_t nk = (d->kv_valid + kBlockN - 1) / kBlockN;
-  const int64_t units = nq * nk;
   if (d->schedule < DIT_SCHED_AUTO || d->schedule > DIT_SCHED_BALANCED)
     return fail(DIT_ERR_INVALID, "schedule=%d is not a dit_schedule", d->schedule);
-  // AUTO resolves to one workgroup per q-tile: on MI355X the balanced
-  // schedule measures no faster yet on the Wan / FLUX / HunyuanVideo shapes
-  // (its partial writes and merges cost what the idle tail of the last
-  // round of workgroups saves), so it runs only when asked for.
-  const bool may_balance = d->schedule == DIT_SCHED_BALANCED;
-  if (may_balance && units > 0 && nq > 0) {
+  // AUTO resolves to one workgroup per q-tile: on MI355X the key-split
+  // schedule measures slower on the Wan / FLUX / HunyuanVideo shapes (each
+  // piece pays a prologue, partial writes and a merge, its L2 reuse is
+  // lower and the clock drops with every CU busy), so it runs only when
+  // asked for.
+  if (d->schedule == DIT_SCHED_BALANCED && nq > 0 && nk >= 2) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       return fail(DIT_ERR_HIP, "cannot query the compute-unit count of the current device");
     const int64_t slots = (int64_t)(512 / dit::kAttnThreads) * cus;   // workgroups resident per CU (two waves per SIMD)
-    // whole rounds of slots, and at least as many workgroups as q-tiles so
-    // a workgroup's run of key tiles spans at most two q-tiles
-    int64_t g = slots * ((nq + slots - 1) / slots);
-    if (g > units / 4) g = units / 4;   // at least 4 key tiles per workgroup
-    if (g < nq) g = nq;
-    if (g > 65535) g = 65535;
-    p.groups = g >= nq ? (int)g : 0;
+    // the best split of at most 8 pieces (pieces of at least 2 key tiles)
+    int64_t best = 1;
+    double best_cost = split_cost(nq, nk, 1, slots);
+    for (int64_t S = 2; S <= 8 && 2 * S <= nk; ++S) {
+      const double c = split_cost(nq, nk, S, slots);
+      if (c < best_cost || best == 1) {
+        best = S;
+        best_cost = c;
+      }
+    }
+    if (nq * best > 0x7fffffffLL) best = 1;
+    p.splits = (int)best;
   }
   size_t off = p.k_bytes;
-  if (p.groups > 0) {
+  if (p.splits > 1) {
+    const size_t pieces = (size_t)nq * p.splits;
     p.part_o_off = off;
-    off += round_up((size_t)2 * p.groups * kThreads * (d->d / 2) * sizeof(float), 256);
+    off += round_up(pieces * kThreads * (d->d / 2) * sizeof(float), 256);
     p.part_l_off = off;
-    off += round_up((size_t)2 * p.groups * kBlockM * sizeof(float), 256);
+    off += round_up(pieces * kBlockM * sizeof(float), 256);
     p.count_off = off;
     p.n_counts = nq;
     off += round_up((size_t)nq * sizeof(int32_t), 256);
-    p.table_off = off;
-    off += round_up((size_t)2 * p.groups * 4 * sizeof(int32_t), 256);
-    p.owners_off = off;
-    off += round_up((size_t)nq * 2 * sizeof(int32_t), 256);
   }
   p.total = off;
   *pl = p;
@@ -241,18 +252,14 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
     p.ks_h = (int64_t)d.s_kv * d.d;
     p.ks_s = d.d;
   }
-  if (pl.groups > 0) {
+  p.sk_splits = pl.splits;
+  if (pl.splits > 1) {
     char *ws = static_cast<char *>(d.workspace);
-    p.sk_groups = pl.groups;
     p.sk_part_o = reinterpret_cast<float *>(ws + pl.part_o_off);
     p.sk_part_l = reinterpret_cast<float *>(ws + pl.part_l_off);
     p.sk_count = reinterpret_cast<int32_t *>(ws + pl.count_off);
-    int4 *table = reinterpret_cast<int4 *>(ws + pl.table_off);
-    int2 *owners = reinterpret_cast<int2 *>(ws + pl.owners_off);
-    p.sk_table = table;
-    p.sk_owners = owners;
-    rc = hip_status(dit::launch_sk_plan(table, owners, p.sk_count, pl.groups, (int)pl.n_counts,
-                                        (d.kv_valid + kBlockN - 1) / kBlockN, st), "schedule plan launch");
+    // arrival counters start at zero (a fill kernel, not a memset node)
+    rc = hip_status(dit::launch_zero_i32(p.sk_count, pl.n_counts, st), "counter clear launch");
     if (rc != DIT_OK) return rc;
   }
   return hip_status(dit::launch_attn_fwd(p, d.d, st), "attention launch");

@@ -406,17 +406,6 @@ __device__ __forceinline__ void store_final(const P &p, int b, int h, int qrow, 
   if (p.lse != nullptr && hf == 0) p.lse[((int64_t)b * p.H + h) * p.s_q + qrow] = row_ok ? lse2 * kLn2 : -INFINITY;
 }
 
-// Balanced schedule: workgroup w owns units [begin(w), begin(w+1)) of the
-// (q-tile, key-tile) space, q-tile major.
-__device__ __forceinline__ int64_t sk_begin(int64_t w, int64_t units, int groups) { return w * units / groups; }
-
-__device__ __forceinline__ int sk_owner(int64_t u, int64_t units, int groups) {
-  int64_t w = (u * groups) / units;
-  while (w + 1 < groups && sk_begin(w + 1, units, groups) <= u) ++w;
-  while (w > 0 && sk_begin(w, units, groups) > u) --w;
-  return (int)w;
-}
-
 // Partials of split q-tiles move between workgroups that may sit on
 // different XCDs (separate L2s), so they are written and read with the
 // agent-coherent cache policy (sc1) instead of through a fence that would
@@ -438,52 +427,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_l_view(const P &p, int sl
                                            0x00020000);
 }
 
-template <class P>
-__device__ __forceinline__ int sk_slot(const P &p, int x, int T) {
-  return 2 * x + (p.sk_table[2 * x].x == T ? 0 : 1);
-}
-
-// The last piece of q-tile T to finish combines all pieces (written by
-// workgroups own.x..own.y; its own one is still in registers as the
-// normalised o = acc / l with log2 LSE lse2) and writes the final O and LSE:
-// O = sum_x w_x o_x / sum_x w_x with w_x = 2^(lse_x - M), M = max_x lse_x.
-// The pieces are combined in workgroup order whichever of them finished
-// last, so the result is the same bits on every call.
+// The last piece of q-tile T to finish combines all S pieces (slot T*S + s
+// holds piece s; this workgroup's own piece `own` is still in registers as
+// the normalised o = acc / l with log2 LSE lse2) and writes the final O and
+// LSE: O = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - M), M = max_s
+// lse_s. The pieces are combined in key order whichever finished last, so
+// the result is the same bits on every call.
 template <int D, class P>
-__device__ __forceinline__ void merge_pieces(const P &p, const Lane<D> &ln, int T, int own_slot, int b, int h,
-                                             int qrow, bool row_ok, const f32x16 *o, float lse2) {
+__device__ __forceinline__ void merge_pieces(const P &p, const Lane<D> &ln, int T, int own, int b, int h, int qrow,
+                                             bool row_ok, const f32x16 *o, float lse2) {
   constexpr int DB = D / 32;
-  const int2 own = p.sk_owners[T];
+  const int S = p.sk_splits;
   const int row = ln.wave * 32 + ln.l32;
   float M = -INFINITY;
-  for (int x = own.x; x <= own.y; ++x) {
-    const int sx = sk_slot(p, x, T);
-    const float lx =
-        sx == own_slot ? lse2 : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, sx), row * 4, 0, kSC1));
+  for (int x = 0; x < S; ++x) {
+    const float lx = x == own ? lse2
+                              : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, T * S + x), row * 4,
+                                                                                    0, kSC1));
     M = fmaxf(M, lx);
   }
   float wsum = 0.f;
-  for (int x = own.x; x <= own.y; ++x) {
-    const int sx = sk_slot(p, x, T);
+  for (int x = 0; x < S; ++x) {
     wsum += __builtin_amdgcn_exp2f(
-        (sx == own_slot ? lse2 : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, sx), row * 4, 0, kSC1))) - M);
+        (x == own ? lse2
+                  : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, T * S + x), row * 4, 0, kSC1))) -
+        M);
   }
-  // one 32-channel block at a time, in place over o: the running sum of
-  // the pieces before this workgroup's own one needs only 16 registers
+  // one 32-channel block at a time: the running sum of the pieces before
+  // this workgroup's own one needs only 16 registers
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     f32x16 a = f32x16{};
-    for (int x = own.x; x <= own.y; ++x) {
-      const int sx = sk_slot(p, x, T);
-      if (sx == own_slot) {
+    for (int x = 0; x < S; ++x) {
+      if (x == own) {
         const float wx = __builtin_amdgcn_exp2f(lse2 - M);
 #pragma unroll
         for (int r = 0; r < 16; ++r) a[r] = fmaf(wx, o[db][r], a[r]);
       } else {
-        const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, sx);
+        const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, T * S + x);
         const float wx = __builtin_amdgcn_exp2f(
-            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, sx), row * 4, 0, kSC1)) - M);
+            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, T * S + x), row * 4, 0, kSC1)) - M);
         u32x4 c[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(v, ln.tid * 16, (db * 4 + i) * NT * 16, kSC1);
@@ -537,26 +521,12 @@ __device__ __forceinline__ void make_lane(const P &p, int tid, Lane<D> &ln) {
     const int chunk0 = 2 * (tg & 1) + (tq >> 1);
     ln.vx = vrow * (D * 2) + ((chunk0 ^ G::fv(vrow)) * 16) + 8 * (tq & 1);
   }
-
-}
-
-// The kernel's AttnParams argument (the first explicit argument, at offset 0
-// of the kernel-argument segment) through a pointer the compiler cannot
-// track, so the fields a phase reads are loaded again with scalar loads
-// instead of being kept live in SGPRs from an earlier read.
-typedef const __attribute__((address_space(4))) AttnParams kernarg_params_t;
-__device__ __forceinline__ kernarg_params_t &kernarg_params() {
-  kernarg_params_t *kp = (kernarg_params_t *)__builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(kp));
-  return *kp;
 }
 
 template <int D, bool BALANCED>
 __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   using G = Geo<D>;
-  constexpr int DK = D / 16;
   constexpr int DB = D / 32;
-  constexpr int CPR = G::CPR;
   __shared__ __attribute__((aligned(1024))) char smem[4 * G::TILE_BYTES];
   __shared__ int last_flag;
 
@@ -587,68 +557,49 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
     return;
   }
 
-  // ---- balanced schedule: this workgroup's one or two runs of key tiles,
-  // from the table the planning kernel wrote; q-tiles split between
-  // workgroups are combined by the last piece to finish.
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-#pragma unroll 1
-  for (int seg = 0; seg < 2; ++seg) {
-    // Parameters are re-read from the kernel-argument segment through an
-    // opaque pointer in each phase, and the per-lane constants rebuilt from
-    // an opaque thread id, so nothing but the loop counter stays live in
-    // registers across a run's key loop (SGPR pressure otherwise defeats the
-    // MFMA/VALU interleave of the steady state).
-    kernarg_params_t &pa = kernarg_params();
-    const int4 sg = pa.sk_table[2 * w + seg];   // {q-tile, kb, ke, slot or -1 when the run covers the q-tile}
-    if (sg.x < 0) break;
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    make_lane<D>(pa, tid, ln);
-    {
-      const int qt = sg.x % pa.n_qtiles, bh = sg.x / pa.n_qtiles;
-      run_qtile<D>(pa, smem, ln, bh / pa.H, bh % pa.H, qt, sg.y, sg.z, acc_o, m_run, l_run);
-    }
-    kernarg_params_t &pe = kernarg_params();
-    const int4 se = pe.sk_table[2 * w + seg];
-    const int T = se.x, slot = se.w;
-    const int qt = T % pe.n_qtiles, bh = T / pe.n_qtiles;
-    const int h = bh % pe.H, b = bh / pe.H;
-    const int qrow = qt * BM + ln.wave * 32 + ln.l32;
-    const float l_tot = pair_sum(l_run);
-    const float lse2 = m_run + __log2f(l_tot);
-    const bool row_ok = qrow < pe.q_valid;
-    if (slot < 0) {
-      store_final<D>(pe, b, h, qrow, ln.hf, acc_o, lse2, row_ok ? 1.0f / l_tot : 0.f, row_ok);
-    } else {
-      // partial: O / l (fp32, in this lane's accumulator layout) and log2
-      // LSE, written agent-coherent; the arrival counter is bumped once
-      // every thread's stores completed.
-      const float inv = 1.0f / l_tot;
+  // ---- key-split schedule: piece s of q-tile T covers key tiles
+  // [s*nk/S, (s+1)*nk/S). Blocks are numbered split-major, so the pieces
+  // running together read the same key range (their K/V tiles stay in L2),
+  // and consecutive q-tiles of a head share an XCD. The last piece of a
+  // q-tile to finish merges the others with its own.
+  const int nq_all = p.n_qtiles * p.H * p.B;
+  const int S = p.sk_splits;
+  const int s = blockIdx.x / nq_all;
+  const int T = xcd_remap(blockIdx.x - s * nq_all, nq_all);
+  const int kb = (int)((int64_t)s * nk / S), ke = (int)((int64_t)(s + 1) * nk / S);
+  const int qt = T % p.n_qtiles, bh = T / p.n_qtiles;
+  const int h = bh % p.H, b = bh / p.H;
+  const int qrow = qt * BM + ln.wave * 32 + ln.l32;
+  run_qtile<D>(p, smem, ln, b, h, qt, kb, ke, acc_o, m_run, l_run);
+  const float l_tot = pair_sum(l_run);
+  const float lse2 = m_run + __log2f(l_tot);
+  const bool row_ok = qrow < p.q_valid;
+  // partial: O / l (fp32, in this lane's accumulator layout) and log2 LSE,
+  // written agent-coherent; the arrival counter is bumped once every
+  // thread's stores completed.
+  const int slot = T * S + s;
+  const float inv = 1.0f / l_tot;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc_o[db] *= inv;
-      const __amdgpu_buffer_rsrc_t v = part_o_view<D>(pe, slot);
+  for (int db = 0; db < DB; ++db) acc_o[db] *= inv;
+  const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, slot);
 #pragma unroll
-      for (int j = 0; j < DB * 4; ++j) {
-        const int db = j >> 2, r = 4 * (j & 3);
-        const u32x4 c = {__float_as_uint(acc_o[db][r]), __float_as_uint(acc_o[db][r + 1]),
-                         __float_as_uint(acc_o[db][r + 2]), __float_as_uint(acc_o[db][r + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(c, v, ln.tid * 16, j * NT * 16, kSC1);
-      }
-      if (ln.hf == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), part_l_view(pe, slot), (ln.wave * 32 + ln.l32) * 4, 0, kSC1);
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial is in coherent memory
-      __syncthreads();
-      if (ln.tid == 0) {
-        const int2 own = pe.sk_owners[T];     // workgroups owning the pieces of q-tile T
-        const int old = __hip_atomic_fetch_add(pe.sk_count + T, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (old == own.y - own.x) ? 1 : 0;
-        if (last_flag) __hip_atomic_store(pe.sk_count + T, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();
-      if (last_flag) merge_pieces<D>(pe, ln, T, slot, b, h, qrow, row_ok, acc_o, lse2);
-    }
-    __syncthreads();   // LDS and last_flag are reused by the next run
+  for (int j = 0; j < DB * 4; ++j) {
+    const int db = j >> 2, r = 4 * (j & 3);
+    const u32x4 c = {__float_as_uint(acc_o[db][r]), __float_as_uint(acc_o[db][r + 1]),
+                     __float_as_uint(acc_o[db][r + 2]), __float_as_uint(acc_o[db][r + 3])};
+    __builtin_amdgcn_raw_buffer_store_b128(c, v, ln.tid * 16, j * NT * 16, kSC1);
   }
+  if (ln.hf == 0)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), part_l_view(p, slot), (ln.wave * 32 + ln.l32) * 4, 0, kSC1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial is in coherent memory
+  __syncthreads();
+  if (ln.tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.sk_count + T, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = (old == S - 1) ? 1 : 0;
+    if (last_flag) __hip_atomic_store(p.sk_count + T, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (last_flag) merge_pieces<D>(p, ln, T, s, b, h, qrow, row_ok, acc_o, lse2);
 }
 
 // K rotation pre-pass: head (blockIdx.y, blockIdx.z) rows s < valid, one
@@ -673,46 +624,24 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
   }
 }
 
-__global__ __launch_bounds__(256) void sk_plan_kernel(int4 *table, int2 *owners, int32_t *count, int groups,
-                                                      int n_qt, int nk) {
-  const int64_t units = (int64_t)n_qt * nk;
-  for (int w = blockIdx.x * blockDim.x + threadIdx.x; w < groups; w += gridDim.x * blockDim.x) {
-    const int64_t u0 = sk_begin(w, units, groups), u1 = sk_begin(w + 1, units, groups);
-    // groups >= n_qt, so a run is at most one q-tile long and a workgroup
-    // has at most two runs; a run covering its whole q-tile needs no slot
-    int4 r[2] = {make_int4(-1, 0, 0, -1), make_int4(-1, 0, 0, -1)};
-    int n = 0;
-    for (int64_t u = u0; u < u1 && n < 2; ++n) {
-      const int T = (int)(u / nk), kb = (int)(u % nk);
-      const int ke = (int)((u1 - u < (int64_t)(nk - kb)) ? kb + (u1 - u) : nk);
-      const bool full = (kb == 0 && ke == nk);
-      r[n] = make_int4(T, kb, ke, full ? -1 : 2 * w + n);
-      u += ke - kb;
-    }
-    table[2 * w] = r[0];
-    table[2 * w + 1] = r[1];
-  }
-  for (int T = blockIdx.x * blockDim.x + threadIdx.x; T < n_qt; T += gridDim.x * blockDim.x) {
-    owners[T] = make_int2(sk_owner((int64_t)T * nk, units, groups), sk_owner((int64_t)(T + 1) * nk - 1, units, groups));
-    count[T] = 0;
-  }
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
 }  // namespace
 
-hipError_t launch_sk_plan(int4 *table, int2 *owners, int32_t *count, int groups, int n_qt, int nk,
-                          hipStream_t stream) {
-  const int n = groups > n_qt ? groups : n_qt;
-  int blocks = (n + 255) / 256;
+hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
   if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(sk_plan_kernel, dim3(blocks), dim3(256), 0, stream, table, owners, count, groups, n_qt, nk);
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream) {
-  const int64_t nblocks = p.sk_groups > 0 ? (int64_t)p.sk_groups : (int64_t)p.n_qtiles * p.H * p.B;
+  const bool bal = p.sk_splits > 1;
+  const int64_t nblocks = (int64_t)p.n_qtiles * p.H * p.B * (bal ? p.sk_splits : 1);
   if (nblocks <= 0) return hipSuccess;
-  const bool bal = p.sk_groups > 0;
   if (d == 128) {
     if (bal) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
     else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);

@@ -48,14 +48,13 @@ struct AttnParams {
   int32_t o_f32;
   int32_t n_qtiles;
   float scale_log2;  // sm_scale * log2(e)
-  // balanced schedule (sk_groups > 0): workgroup w owns a contiguous run of
-  // (q-tile, key-tile) units; split q-tiles meet in the workspace below
-  int32_t sk_groups;
-  float *sk_part_o;  // [2 * sk_groups][kAttnThreads][d/2] partial O / l, fp32
-  float *sk_part_l;  // [2 * sk_groups][kAttnBlockM rows] partial LSE, log2 units
-  int32_t *sk_count; // [B * H * n_qtiles] arrival counters, zero on entry
-  const int4 *sk_table;  // [2 * sk_groups] runs {q-tile, kb, ke, slot or -1}
-  const int2 *sk_owners; // [B * H * n_qtiles] first and last workgroup of each q-tile
+  // key-split schedule (sk_splits > 1): the keys of every q-tile are cut
+  // into sk_splits contiguous ranges, one workgroup each; pieces meet in the
+  // workspace below
+  int32_t sk_splits;
+  float *sk_part_o;  // [q-tiles * sk_splits][kAttnThreads][d/2] partial O / l, fp32
+  float *sk_part_l;  // [q-tiles * sk_splits][kAttnBlockM rows] partial LSE, log2 units
+  int32_t *sk_count; // [q-tiles] arrival counters, zero on entry (left zero on exit)
 };
 
 // Parameters of the K rotation pre-pass.
@@ -87,8 +86,7 @@ struct TableParams {
 
 // Launchers (host side, defined next to their kernels). Return hipError_t.
 hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream);
-hipError_t launch_sk_plan(int4 *table, int2 *owners, int32_t *count, int groups, int n_qt, int nk,
-                          hipStream_t stream);
+hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t stream);
 hipError_t launch_rope_rotate(const RopeRotateParams &p, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 hipError_t launch_rope_tables(const TableParams &p, hipStream_t stream);

@@ -327,8 +327,8 @@ def test_pad_unpad_round_trip(ops):
     dict(name="flux", sched=1),
 ])
 def test_forced_schedules_match_oracle(ops, case):
-    """Both work schedules (one workgroup per query tile; balanced runs of
-    key tiles with split tiles combined in the workspace) against the oracle."""
+    """Both work schedules (one workgroup per query tile; key ranges split
+    into pieces merged in the workspace) against the oracle."""
     import torch
     w = W.WORKLOADS[case["name"]]
     say(f"schedule {case['sched']} {w.name}")
