@@ -2,8 +2,8 @@
 
 One step = one pass of the whole path over one batch of synthetic tokens:
   RoPE tables from positions -> tail pad of Q, K, V tokens ([B, S, H, d]) ->
-  attention forward (K rotation pre-pass + the fused attention kernel, Q RoPE
-  fused, pad keys masked) -> unpad of O.
+  attention forward (Q / K rotation pre-pass + the attention kernel, pad
+  keys masked) -> unpad of O.
 Inputs are resident in HBM before timing starts. Throughput is counted over
 valid tokens: FLOP = 4 * B * H * S_valid^2 * d per step.
 
@@ -125,8 +125,8 @@ def read_traffic():
 
 # ------------------------------------------------------- counter workflow
 def pmc_target(args):
-    """Launch the dominant kernel (attention with K already rotated) and the
-    calibration copy a few times each; nothing else runs on the GPU."""
+    """Launch the dominant kernel (attention without the rotation pre-pass)
+    and the calibration copy a few times each; nothing else runs on the GPU."""
     import numpy as np
     import torch
     import workloads as W
@@ -139,7 +139,7 @@ def pmc_target(args):
     o = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev)
     for _ in range(5):
-        ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=(cos, sin), rope_k=None, out=o, lse=lse)
+        ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=None, rope_k=None, out=o, lse=lse)
     src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
     src.fill_(1)
     dst = torch.empty_like(src)
@@ -175,7 +175,7 @@ def traffic_summary(args):
     f_fac = COPY_CAL_BYTES / (fetch["copy"] * 1024.0)
     w_fac = COPY_CAL_BYTES / (write["copy"] * 1024.0)
     rec = {
-        "kernel": "attn_fwd_kernel<128, false> (wan480, K pre-rotated)",
+        "kernel": "attn_fwd_kernel<128, false> (wan480, Q and K pre-rotated)",
         "kernel_source_sha256_16": kernel_source_hash(),
         "fetch_kib_per_launch_raw": fetch["attn"], "write_kib_per_launch_raw": write["attn"],
         "copy_fetch_kib_raw": fetch["copy"], "copy_write_kib_raw": write["copy"],
@@ -194,8 +194,8 @@ def traffic_summary(args):
 
 # -------------------------------------------------------------- the bench
 def config_table(np, torch, ops, W, dev, n_iter):
-    """Attention throughput on every config (dit_attn_fwd call = K rotation
-    pre-pass + fused kernel; the Wan 720p config also as 4 key shards plus
+    """Attention throughput on every config (dit_attn_fwd call = Q / K
+    rotation pre-pass + attention kernel; the Wan 720p config also as 4 key shards plus
     dit_lse_merge)."""
     res = {}
     for name in ("tiny", "flux", "wan480", "hunyuan", "wan720"):
@@ -306,12 +306,15 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # Dominant kernel alone: with K already rotated, dit_attn_fwd launches
-    # exactly one kernel (the fused attention kernel) per call.
-    k_rot = ws[: B * H * Sp * d * 2].view(torch.bfloat16).view(B, H, Sp, d).clone()
+    # Dominant kernel alone: with Q and K already rotated (the copies the
+    # pre-pass left in the workspace: K first, then Q), dit_attn_fwd launches
+    # exactly one kernel (the attention kernel) per call.
+    n_el = B * H * Sp * d
+    k_rot = ws[: n_el * 2].view(torch.bfloat16).view(B, H, Sp, d).clone()
+    q_rot = ws[n_el * 2: n_el * 4].view(torch.bfloat16).view(B, H, Sp, d).clone()
 
     def attn_only():
-        ops.attn_fwd(qv, k_rot, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=None,
+        ops.attn_fwd(q_rot, k_rot, vv, q_valid=Sv, kv_valid=Sv, rope_q=None, rope_k=None,
                      out=op.transpose(1, 2), lse=lse)
 
     n = args.kernel_iters
@@ -344,13 +347,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "B": B, "H": H, "d": d, "s_valid": Sv, "s_pad": Sp,
                    "flop_per_step": flop,
-                   "step": "tables + pad(Q,K,V) + attn_fwd(K-rope pre-pass + fused kernel) + unpad(O)"},
+                   "step": "tables + pad(Q,K,V) + attn_fwd(Q/K RoPE pre-pass + attention kernel) + unpad(O)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch", "traffic_source": traffic_src,
                      "algorithmic_flop_per_launch": flop, "kernel": "attn_fwd_kernel<128, false>",
                      "kernel_us": us_attn},
-        "kernels_us": {"attn_fwd_kernel": us_attn, "dit_attn_fwd_call(K pre-pass + kernel)": us_call,
+        "kernels_us": {"attn_fwd_kernel": us_attn, "dit_attn_fwd_call(Q/K pre-pass + kernel)": us_call,
                        "rope_tables": us_tables, "pad_tokens(one tensor)": us_pad, "unpad_tokens": us_unpad,
                        "pad_GBps": pad_bytes / (us_pad * 1e-6) / 1e9,
                        "unpad_GBps": 2 * Sv * H * d * 2 * B / (us_unpad * 1e-6) / 1e9},

@@ -87,7 +87,8 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * bf16 (round to nearest even). cos_q/sin_q are fp32 [s_q, d/2] tables for
  * the query rows, cos_k/sin_k fp32 [s_kv, d/2] for the key rows (for a key
  * shard, pass the table pointers offset to the shard's first row). Each pair
- * must be both NULL (no rotation) or both non-NULL.
+ * must be both NULL (no rotation) or both non-NULL. With rotation, B * H may
+ * not exceed 262140 (else DIT_ERR_UNSUPPORTED).
  *
  * Scores are sm_scale * <q'_i, k'_j> (sm_scale == 0 selects 1/sqrt(d); it
  * must be finite and positive). Both contractions run on bf16 MFMA with fp32
@@ -97,7 +98,8 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * result that dit_lse_merge will combine), written for rows [0, s_q).
  * lse: fp32 dense [B, H, s_q], natural log, or NULL to skip it.
  *
- * workspace: device scratch for the once-per-call K rotation and, under the
+ * workspace: device scratch for the once-per-call rotated copies of K and Q
+ * (dense bf16 [B, H, s, d] each, when their tables are given) and, under the
  * BALANCED schedule, the partial results of split query tiles and their
  * arrival counters. Required (non-NULL, 256-byte aligned, at least
  * dit_attn_workspace_size() bytes) when that size is non-zero. The caller

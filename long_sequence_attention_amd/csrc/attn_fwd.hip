@@ -1,6 +1,6 @@
 // Attention forward for gfx950: bf16 MFMA (v_mfma_f32_32x32x16_bf16) with
 // fp32 accumulation, online softmax in exp2 form, exact tail-pad masking,
-// split-halves RoPE fused into the Q load, and a K rotation pre-pass.
+// and a split-halves RoPE pre-pass that rotates Q and K once per call.
 //
 // What is computed (the pages' problem statement): for each (b, h) and query
 // row i < q_valid, O_i = sum_{j < kv_valid} softmax_j(scale * q'_i . k'_j) v_j
@@ -13,7 +13,7 @@
 //   * Each wave owns 32 query rows and computes S^T = K Q^T, so a lane holds
 //     16 scores of ONE query (lane % 32) per 32-key block: the row max is an
 //     in-register reduction plus one v_permlane32_swap with lane ^ 32.
-//   * Q stays in registers (bf16, rotated once) as the B operand of S^T.
+//   * Q stays in registers (bf16, already rotated) as the B operand of S^T.
 //   * K and V tiles (64 keys x d) move HBM -> LDS with buffer loads that
 //     write LDS directly (no VGPR staging). Each load's buffer view ends at
 //     row kv_valid, so tail pads and rows past the tensor arrive as zeros:
@@ -62,13 +62,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 __device__ __forceinline__ u32x4 ldg16(const bf16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-__device__ __forceinline__ void rotate8(u32x4 &lo, u32x4 &hi, const float *c, const float *s) {
-  const float4 c0 = *reinterpret_cast<const float4 *>(c);
-  const float4 c1 = *reinterpret_cast<const float4 *>(c + 4);
-  const float4 s0 = *reinterpret_cast<const float4 *>(s);
-  const float4 s1 = *reinterpret_cast<const float4 *>(s + 4);
-  const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+// Split-halves rotation of 8 channel pairs (lo holds channels i..i+7 of the
+// first half, hi the partners d/2 later) in fp32, rounded once to bf16.
+__device__ __forceinline__ void rotate8(u32x4 &lo, u32x4 &hi, const float *cv, const float *sv) {
   u32x4 nlo, nhi;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -332,15 +328,6 @@ __device__ __forceinline__ void run_qtile(const P &p, char *smem, const Lane<D> 
     const bf16_t *qr = qbase + (int64_t)(in_q ? qrow : 0) * p.qs_s;
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) raw[dk] = in_q ? ldg16(qr + dk * 16 + ln.hf * 8) : u32x4{0u, 0u, 0u, 0u};
-    if (p.cos_q != nullptr) {
-      // pair (i, i + D/2) lives in (dk, dk + DK/2) of the same lane
-      const int64_t trow = (int64_t)(in_q ? qrow : 0) * (D / 2);
-#pragma unroll
-      for (int dk = 0; dk < DK / 2; ++dk) {
-        const int i0 = dk * 16 + ln.hf * 8;
-        rotate8(raw[dk], raw[dk + DK / 2], p.cos_q + trow + i0, p.sin_q + trow + i0);
-      }
-    }
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) qop[dk] = __builtin_bit_cast(bf16x8, raw[dk]);
   }
@@ -602,25 +589,53 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   if (last_flag) merge_pieces<D>(p, ln, T, s, b, h, qrow, row_ok, acc_o, lse2);
 }
 
-// K rotation pre-pass: head (blockIdx.y, blockIdx.z) rows s < valid, one
-// thread per 8-channel run of the first half and its partner run d/2 later.
+// Rotation pre-pass of Q and K (blockIdx.y picks the tensor). A thread owns
+// one 8-channel run of the first half of a row and its partner run d/2
+// later: it loads that row's 16 table values once and applies them to the
+// row of up to kRopeHeads (b, h) pairs (blockIdx.z picks the group), so the
+// tables are read once per row and head group rather than once per head.
 // RUNS = d/16 threads per row, 256/RUNS rows per block iteration.
+constexpr int kRopeHeads = 4;
+
 template <int RUNS>
 __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
   constexpr int ROWS = 256 / RUNS, HALF = RUNS * 8;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const RopeSeg &g = p.seg[blockIdx.y];
   const int c = threadIdx.x % RUNS;
-  const bf16_t *xh = p.x + b * p.xs_b + h * p.xs_h;
-  bf16_t *yh = p.y + ((int64_t)b * p.H + h) * p.S * (2 * HALF);
-  for (int s = blockIdx.x * ROWS + threadIdx.x / RUNS; s < p.valid; s += gridDim.x * ROWS) {
-    const bf16_t *xr = xh + (int64_t)s * p.xs_s;
-    bf16_t *yr = yh + (int64_t)s * (2 * HALF);
-    u32x4 lo = ldg16(xr + c * 8);
-    u32x4 hi = ldg16(xr + HALF + c * 8);
+  const int nbh = p.B * p.H;
+  const int bh0 = blockIdx.z * kRopeHeads;
+  const int nh = nbh - bh0 < kRopeHeads ? nbh - bh0 : kRopeHeads;
+  for (int s = blockIdx.x * ROWS + threadIdx.x / RUNS; s < g.rows; s += gridDim.x * ROWS) {
     const int64_t to = (int64_t)s * HALF + c * 8;
-    rotate8(lo, hi, p.cos_t + to, p.sin_t + to);
-    *reinterpret_cast<u32x4 *>(yr + c * 8) = lo;
-    *reinterpret_cast<u32x4 *>(yr + HALF + c * 8) = hi;
+    float cv[8], sv[8];
+    {
+      const float4 c0 = *reinterpret_cast<const float4 *>(g.cos_t + to);
+      const float4 c1 = *reinterpret_cast<const float4 *>(g.cos_t + to + 4);
+      const float4 s0 = *reinterpret_cast<const float4 *>(g.sin_t + to);
+      const float4 s1 = *reinterpret_cast<const float4 *>(g.sin_t + to + 4);
+      cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w; cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
+      sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+    }
+    // all loads of the group first, then the rotations and stores
+    u32x4 lo[kRopeHeads], hi[kRopeHeads];
+#pragma unroll
+    for (int j = 0; j < kRopeHeads; ++j) {
+      if (j < nh) {
+        const int bh = bh0 + j, b = bh / p.H, h = bh - b * p.H;
+        const bf16_t *xr = g.x + b * g.xs_b + h * g.xs_h + (int64_t)s * g.xs_s;
+        lo[j] = ldg16(xr + c * 8);
+        hi[j] = ldg16(xr + HALF + c * 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRopeHeads; ++j) {
+      if (j < nh) {
+        rotate8(lo[j], hi[j], cv, sv);
+        bf16_t *yr = g.y + ((int64_t)(bh0 + j) * g.S + s) * (2 * HALF);
+        *reinterpret_cast<u32x4 *>(yr + c * 8) = lo[j];
+        *reinterpret_cast<u32x4 *>(yr + HALF + c * 8) = hi[j];
+      }
+    }
   }
 }
 
@@ -653,14 +668,15 @@ hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream) {
 }
 
 hipError_t launch_rope_rotate(const RopeRotateParams &p, hipStream_t stream) {
-  if ((int64_t)p.B * p.H * p.valid <= 0) return hipSuccess;
+  int rows = 0;
+  for (int i = 0; i < p.n_seg; ++i) rows = p.seg[i].rows > rows ? p.seg[i].rows : rows;
+  const int64_t nbh = (int64_t)p.B * p.H;
+  if (p.n_seg <= 0 || rows <= 0 || nbh <= 0) return hipSuccess;
   const int runs = p.d / 16;
-  const int rows = 256 / runs;
-  int bx = (p.valid + rows - 1) / rows;
-  // about 2048 blocks in all, each striding over its head's rows
-  const int cap = (int)((2048 + (int64_t)p.B * p.H - 1) / ((int64_t)p.B * p.H));
-  if (bx > cap) bx = cap < 1 ? 1 : cap;
-  const dim3 grid((unsigned)bx, (unsigned)p.H, (unsigned)p.B);
+  const int per_block = 256 / runs;
+  int64_t bx = (rows + per_block - 1) / per_block;
+  if (bx > 65535) bx = 65535;   // the kernel strides over the remaining rows
+  const dim3 grid((unsigned)bx, (unsigned)p.n_seg, (unsigned)((nbh + kRopeHeads - 1) / kRopeHeads));
   if (runs == 8) hipLaunchKernelGGL(rope_rotate_kernel<8>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(rope_rotate_kernel<4>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();

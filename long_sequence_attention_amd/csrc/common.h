@@ -43,7 +43,6 @@ struct AttnParams {
   int64_t ks_b, ks_h, ks_s;
   int64_t vs_b, vs_h, vs_s;
   int64_t os_b, os_h, os_s;
-  const float *cos_q, *sin_q;
   int32_t B, H, s_q, s_kv, q_valid, kv_valid;
   int32_t o_f32;
   int32_t n_qtiles;
@@ -57,13 +56,21 @@ struct AttnParams {
   int32_t *sk_count; // [q-tiles] arrival counters, zero on entry (left zero on exit)
 };
 
-// Parameters of the K rotation pre-pass.
-struct RopeRotateParams {
+// One tensor of the rotation pre-pass: rows [0, rows) of x ((b, h, s)
+// strides in elements) rotated into the dense [B, H, S, d] buffer y with the
+// fp32 [>= rows, d/2] tables cos_t / sin_t.
+struct RopeSeg {
   const bf16_t *x;
-  bf16_t *y;  // dense [B, H, S, d]
+  bf16_t *y;
   const float *cos_t, *sin_t;
   int64_t xs_b, xs_h, xs_s;
-  int32_t B, H, S, valid, d;
+  int32_t S, rows;
+};
+
+// Parameters of the Q / K rotation pre-pass (one launch for both tensors).
+struct RopeRotateParams {
+  RopeSeg seg[2];
+  int32_t n_seg, B, H, d;
 };
 
 constexpr int kMaxMergeParts = 16;
