@@ -232,21 +232,23 @@ def _edge(ops, seed, B, H, s_q, s_kv, d, q_valid, kv_valid, q_scale=1.0, rope=Tr
     v[:, :, kv_valid:] = W.finite_garbage_bits(r, v[:, :, kv_valid:].shape)
     pq = r.integers(0, 60, (s_q, 1)).astype(np.int32)
     pk = r.integers(0, 60, (s_kv, 1)).astype(np.int32)
-    if rope:
-        tq = ops.rope_split_tables(torch.from_numpy(pq).to(dev()), (d,), d, 10000.0)
-        tk = ops.rope_split_tables(torch.from_numpy(pk).to(dev()), (d,), d, 10000.0)
-    else:
-        tq = tk = None
+    # rope: True (Q and K), False (neither), "q" or "k" (that tensor only)
+    rot_q, rot_k = rope in (True, "q"), rope in (True, "k")
+    tq = ops.rope_split_tables(torch.from_numpy(pq).to(dev()), (d,), d, 10000.0) if rot_q else None
+    tk = ops.rope_split_tables(torch.from_numpy(pk).to(dev()), (d,), d, 10000.0) if rot_k else None
     o, l = ops.attn_fwd(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), q_valid=q_valid, kv_valid=kv_valid,
                         rope_q=tq, rope_k=tk)
     torch.cuda.synchronize()
     qf, kf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(k)
-    if rope:
+    if rope is True:
         O_ref, L_ref = oracle.dit_path(q, k, v, pq, pk, (d,), 10000.0, q_valid, kv_valid)
+    if rot_q:
         cq, sq = oracle.rope_tables(pq, (d,), 10000.0)
+        qf = oracle.rope_split_halves(qf, cq, sq)
+    if rot_k:
         ck, sk = oracle.rope_tables(pk, (d,), 10000.0)
-        qf, kf = oracle.rope_split_halves(qf, cq, sq), oracle.rope_split_halves(kf, ck, sk)
-    else:
+        kf = oracle.rope_split_halves(kf, ck, sk)
+    if rope is not True:
         O_ref, L_ref = oracle.attention(qf, kf, oracle.bf16_to_f64(v), q_valid, kv_valid)
     bound = lse_rounding_bound(qf, kf, kv_valid, 1.0 / math.sqrt(d))
     # the oracle again on the rotated Q/K rounded to bf16 (the rounding the
@@ -264,6 +266,8 @@ def _edge(ops, seed, B, H, s_q, s_kv, d, q_valid, kv_valid, q_scale=1.0, rope=Tr
     dict(B=1, H=1, s_q=64, s_kv=64, d=128, q_valid=64, kv_valid=1),         # one valid key
     dict(B=1, H=2, s_q=256, s_kv=192, d=128, q_valid=1, kv_valid=192),      # one valid query
     dict(B=1, H=2, s_q=300, s_kv=1000, d=128, q_valid=299, kv_valid=999, rope=False),
+    dict(B=2, H=5, s_q=333, s_kv=200, d=128, q_valid=333, kv_valid=190, rope="q"),   # RoPE on Q only
+    dict(B=1, H=3, s_q=96, s_kv=450, d=64, q_valid=90, kv_valid=449, rope="k"),      # RoPE on K only
 ])
 def test_edge_shapes(ops, case):
     say(f"edge {case}")
@@ -300,6 +304,13 @@ def test_no_valid_keys_gives_zero_and_minus_inf(ops):
     q = to_dev_bf16(W.bf16_bits(r.standard_normal((1, 2, 100, 128)).astype(np.float32)))
     k = to_dev_bf16(W.finite_garbage_bits(r, (1, 2, 64, 128)))
     o, l = ops.attn_fwd(q, k, k, q_valid=100, kv_valid=0)
+    torch.cuda.synchronize()
+    assert (to_np_f64(o) == 0).all() and np.isneginf(to_np_f64(l)).all()
+    # with RoPE tables: nothing to rotate, no workspace needed, same result
+    tq = ops.rope_split_tables(torch.zeros((100, 1), dtype=torch.int32, device=dev()), (128,), 128, 10000.0)
+    tk = ops.rope_split_tables(torch.zeros((64, 1), dtype=torch.int32, device=dev()), (128,), 128, 10000.0)
+    assert ops.attn_workspace_size(q, k, k, q_valid=100, kv_valid=0, rope_q=tq, rope_k=tk) == 0
+    o, l = ops.attn_fwd(q, k, k, q_valid=100, kv_valid=0, rope_q=tq, rope_k=tk)
     torch.cuda.synchronize()
     assert (to_np_f64(o) == 0).all() and np.isneginf(to_np_f64(l)).all()
 
