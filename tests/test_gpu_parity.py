@@ -59,10 +59,26 @@ def test_rope_tables_match_oracle(ops, name):
     say(f"tables {name}")
     c, s = gpu_tables(ops, w)
     cr, sr = oracle.rope_tables(W.positions(w), w.axes, w.theta)
-    assert np.abs(to_np_f64(c) - cr).max() < 1e-6
-    assert np.abs(to_np_f64(s) - sr).max() < 1e-6
+    # cos/sin evaluated in fp64 and rounded once to fp32: within half an fp32
+    # ulp of values in [-1, 1] (2^-25), plus the oracle's own fp64 error
+    assert np.abs(to_np_f64(c) - cr).max() <= 2.0 ** -25 + 1e-12
+    assert np.abs(to_np_f64(s) - sr).max() <= 2.0 ** -25 + 1e-12
     n_grid = int(np.prod(w.grid))
     assert (to_np_f64(c)[n_grid:] == 1).all() and (to_np_f64(s)[n_grid:] == 0).all()
+
+
+def test_rope_tables_large_and_negative_positions(ops):
+    """Angles far outside [-pi, pi] (positions up to 2^21, and negative ones):
+    fp64 evaluation rounded once to fp32 stays within half an fp32 ulp."""
+    import torch
+    say("tables, large positions")
+    r = np.random.default_rng(48)
+    pos = np.concatenate([r.integers(-(1 << 21), 1 << 21, (500, 2)), np.zeros((12, 2), np.int64)]).astype(np.int32)
+    cos, sin = ops.rope_split_tables(torch.from_numpy(pos).to(dev()), (64, 64), 128, 10000.0)
+    cr, sr = oracle.rope_tables(pos, (64, 64), 10000.0)
+    assert np.abs(to_np_f64(cos) - cr).max() <= 2.0 ** -25 + 1e-12
+    assert np.abs(to_np_f64(sin) - sr).max() <= 2.0 ** -25 + 1e-12
+    assert (to_np_f64(cos)[500:] == 1).all() and (to_np_f64(sin)[500:] == 0).all()
 
 
 # ------------------------------------------------------------------ full configs
