@@ -195,23 +195,28 @@ def traffic_summary(args):
 # -------------------------------------------------------------- the bench
 def config_table(np, torch, ops, W, dev, n_iter):
     """Attention throughput on every config (dit_attn_fwd call = Q / K
-    rotation pre-pass + attention kernel; the Wan 720p config also as 4 key shards plus
+    rotation pre-pass + attention kernel, or the kernel alone for the
+    cross-attention config, which has no RoPE; the Wan 720p config also as 4 key shards plus
     dit_lse_merge)."""
     res = {}
-    for name in ("tiny", "flux", "wan480", "hunyuan", "wan720"):
+    for name in ("tiny", "flux", "wan480", "hunyuan", "wan720", "xattn480"):
         w = W.WORKLOADS[name]
         _, (qd, kd, vd) = dev_tensors(w, np, torch, dev)
         cos, sin = ops.rope_split_tables(torch.from_numpy(W.positions(w)).to(dev), w.axes, w.d, w.theta)
+        tabs = (cos, sin) if w.rope else None
         o = torch.empty_like(qd)
         lse = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid,
-                                                     rope_q=(cos, sin), rope_k=(cos, sin)), 256),
+        ws = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
+                                                     rope_q=tabs, rope_k=tabs), 256),
                          dtype=torch.uint8, device=dev)
         n = max(3, n_iter if w.valid_flop < 1e12 else 3)
-        us = time_us(torch, lambda: ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid,
-                                                 rope_q=(cos, sin), rope_k=(cos, sin), out=o, lse=lse,
+        us = time_us(torch, lambda: ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
+                                                 rope_q=tabs, rope_k=tabs, out=o, lse=lse,
                                                  workspace=ws), n)
         ent = {"us": us, "tflops": w.valid_flop / us / 1e6, "pct_peak": w.valid_flop / us / 1e6 / PEAK_BF16_TFLOPS * 100}
+        if w.kv_valid:   # short-KV: report the HBM side too (Q, K, V, O, LSE once each)
+            nbytes = w.B * w.H * (2 * w.s_pad * w.d * 2 + 2 * w.k_pad * w.d * 2 + w.s_pad * 4)
+            ent.update({"hbm_bytes": nbytes, "hbm_GBps": nbytes / us / 1e3})
         if w.n_key_shards > 1:
             shards = W.key_shards(w)
             po = [torch.empty((w.B, w.H, w.s_pad, w.d), dtype=torch.float32, device=dev) for _ in shards]

@@ -96,6 +96,32 @@ def test_parity_full_config(ops, name):
     assert_pad_rows(og, lg, valid, name)
 
 
+def test_short_kv_cross_attention(ops):
+    """Video queries over 512 text keys (no RoPE): the short-KV regime of the
+    Wan cross-attention (maxdiffusion PR #491, fused short-KV cross-attention
+    kernel), graded at the same bar; then the text padded to 576 rows with
+    garbage (kv_valid = 512) gives the same bits."""
+    import torch
+    w = W.WORKLOADS["xattn480"]
+    say(f"cross-attention {w.s_valid}->{w.s_pad} queries x {w.k_valid} keys, H={w.H}")
+    q, k, v = W.make_qkv(w)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    o, l = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(oracle.bf16_to_f64(q), oracle.bf16_to_f64(k), oracle.bf16_to_f64(v),
+                                    w.s_valid, w.k_valid)
+    valid = np.arange(w.s_pad) < w.s_valid
+    og, lg = to_np_f64(o), to_np_f64(l)
+    compare(og, lg, O_ref, L_ref, valid, "xattn480")
+    assert_pad_rows(og, lg, valid, "xattn480")
+    r = np.random.default_rng(49)
+    kp = np.concatenate([k, W.finite_garbage_bits(r, (w.B, w.H, 64, w.d))], axis=2)
+    vp = np.concatenate([v, W.finite_garbage_bits(r, (w.B, w.H, 64, w.d))], axis=2)
+    o2, l2 = ops.attn_fwd(qd, to_dev_bf16(kp), to_dev_bf16(vp), q_valid=w.s_valid, kv_valid=w.k_valid)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_bits(o2), raw_bits(o)) and np.array_equal(raw_bits(l2), raw_bits(l))
+
+
 @pytest.mark.parametrize("name", ["tiny", "wan480", "hunyuan"])
 def test_pad_invariance_bit_exact(ops, name):
     import torch

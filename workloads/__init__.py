@@ -45,15 +45,28 @@ class Workload:
     theta: float = 10000.0
     n_key_shards: int = 1
     description: str = ""
+    # cross-attention: keys/values of their own length (0 = the query
+    # tokens themselves), and whether RoPE applies at all
+    kv_valid: int = 0
+    kv_pad: int = 0
+    rope: bool = True
 
     @property
     def n_axes(self) -> int:
         return len(self.axes)
 
     @property
+    def k_valid(self) -> int:
+        return self.kv_valid or self.s_valid
+
+    @property
+    def k_pad(self) -> int:
+        return self.kv_pad or self.s_pad
+
+    @property
     def valid_flop(self) -> float:
-        """4*B*H*S_valid^2*d: two dense contractions over valid tokens."""
-        return 4.0 * self.B * self.H * self.s_valid * self.s_valid * self.d
+        """4*B*H*S_valid*K_valid*d: two dense contractions over valid tokens."""
+        return 4.0 * self.B * self.H * self.s_valid * self.k_valid * self.d
 
 
 WORKLOADS = {
@@ -77,6 +90,11 @@ WORKLOADS = {
         "wan720", B=1, H=10, d=128, s_valid=75600, s_pad=75648, axes=(44, 42, 42),
         grid=(21, 45, 80), n_text=0, qk_norm=True, seed=4, n_key_shards=4,
         description="Wan 720p/81f shard: 21x45x80 grid, 75600 padded to 75648, H=10; 4 key shards"),
+    "xattn480": Workload(
+        "xattn480", B=1, H=10, d=128, s_valid=4680, s_pad=4736, axes=(44, 42, 42),
+        grid=(3, 30, 52), n_text=0, qk_norm=True, seed=6, kv_valid=512, kv_pad=512, rope=False,
+        description="Wan 480p short-KV cross-attention: 4680 video queries (padded to 4736) over 512 "
+                    "text keys, H=10 d=128, no RoPE"),
 }
 
 
@@ -143,24 +161,26 @@ def make_head(w: Workload, tensor: str, b: int, h: int, garbage_seed_offset: int
     from the stream seeded by (seed + garbage_seed_offset, tensor index, b, h).
     """
     ti = "qkv".index(tensor)
+    valid, pad = (w.s_valid, w.s_pad) if tensor == "q" else (w.k_valid, w.k_pad)
     rng = np.random.default_rng([w.seed, ti, b, h])
-    x = rng.standard_normal((w.s_valid, w.d), dtype=np.float32)
+    x = rng.standard_normal((valid, w.d), dtype=np.float32)
     if w.qk_norm and tensor in "qk":
         x = _rms_normalise(x)
-    out = np.empty((w.s_pad, w.d), dtype=np.uint16)
-    out[: w.s_valid] = bf16_bits(x)
-    if w.s_pad > w.s_valid:
+    out = np.empty((pad, w.d), dtype=np.uint16)
+    out[:valid] = bf16_bits(x)
+    if pad > valid:
         g = np.random.default_rng([w.seed + garbage_seed_offset, ti, b, h])
-        out[w.s_valid:] = finite_garbage_bits(g, (w.s_pad - w.s_valid, w.d))
+        out[valid:] = finite_garbage_bits(g, (pad - valid, w.d))
     return out
 
 
 def make_qkv(w: Workload, heads=None, garbage_seed_offset: int = 1000):
-    """Q, K, V as bf16 bit arrays (uint16) of shape [B, len(heads), s_pad, d]."""
+    """Q, K, V as bf16 bit arrays (uint16): Q [B, len(heads), s_pad, d], K and V
+    [B, len(heads), k_pad, d]."""
     heads = list(range(w.H)) if heads is None else list(heads)
     res = []
     for t in "qkv":
-        arr = np.empty((w.B, len(heads), w.s_pad, w.d), dtype=np.uint16)
+        arr = np.empty((w.B, len(heads), w.s_pad if t == "q" else w.k_pad, w.d), dtype=np.uint16)
         for b in range(w.B):
             for j, h in enumerate(heads):
                 arr[b, j] = make_head(w, t, b, h, garbage_seed_offset)
