@@ -15,6 +15,9 @@ What each function follows (pages are cited by title and section):
     per-axis frequency schedule is not printed on the pages; the plain
     reading used here is the standard 1-D schedule theta^(-2j/c_a) per axis
     over that axis's own channel count, axes concatenated in pair space.
+  * rms_norm -- the per-head q/k RMS normalisation with a weight vector that
+    precedes RoPE (Difflet PR #153: the FLUX and Wan split-RoPE commits
+    permute the q/k RMSNorm weights along with the channels).
   * attention -- softmax(scale * Q K^T) V over the valid keys only, with the
     natural-log log-sum-exp per query row (mstar PR #376, "Ragged attention
     returns the log-sum-exp": fp32, natural log). Pad keys are dropped
@@ -39,6 +42,7 @@ from .reference import (  # noqa: F401
     rope_split_halves,
     rope_interleaved,
     interleaved_to_split_permutation,
+    rms_norm,
     attention,
     attention_bruteforce,
     lse_merge,

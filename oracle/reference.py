@@ -100,6 +100,22 @@ def rope_interleaved(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndar
     return out
 
 
+def rms_norm(x: np.ndarray, weight, eps: float) -> np.ndarray:
+    """Per-head RMS normalisation over the last axis (d), float64:
+
+        y_c = x_c / sqrt(mean_c' x_c'^2 + eps) * w_c
+
+    The q/k norm that precedes RoPE in the FLUX and Wan attention (Difflet
+    PR #153: the FLUX split-RoPE commit permutes the per-head q/k RMSNorm
+    weights together with the to_q / to_k channels, and the Wan split-RoPE
+    commit does the same). `weight` is [d] in the same channel order as x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * w
+
+
 def interleaved_to_split_permutation(d: int) -> np.ndarray:
     """Channel order [0, 2, ..., d-2, 1, 3, ..., d-1]: x_split = x_inter[..., P]."""
     return np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])

@@ -186,6 +186,49 @@ def test_rope_relative_position_property():
     assert abs(a - b) < 1e-12 * (1 + abs(a))
 
 
+# ------------------------------------------------------------------ q/k RMSNorm
+def test_rms_norm_worked_example():
+    # x = (3, 4): mean of squares 12.5, so y = x / sqrt(12.5); with eps = 0.5
+    # the divisor is sqrt(13) (hand-computed values)
+    y = oracle.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    assert np.allclose(y, [0.848528137423857, 1.131370849898476], rtol=0, atol=1e-15)
+    y = oracle.rms_norm(np.array([3.0, 4.0]), np.array([2.0, -1.0]), 0.5)
+    assert np.allclose(y, [2 * 0.8320502943378437, -1.1094003924504583], rtol=0, atol=1e-15)
+
+
+def test_rms_norm_unit_rms_scale_invariance_and_zero():
+    x = rng(20).standard_normal((3, 5, 128)) * 7.0
+    y = oracle.rms_norm(x, np.ones(128), 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=0, atol=1e-13)
+    assert np.allclose(oracle.rms_norm(0.01 * x, np.ones(128), 0.0), y, rtol=0, atol=1e-12)
+    assert np.allclose(oracle.rms_norm(-x, np.ones(128), 0.0), -y, rtol=0, atol=0)
+    z = oracle.rms_norm(np.zeros((2, 64)), np.ones(64), 1e-6)
+    assert np.isfinite(z).all() and (z == 0).all()
+
+
+def test_rms_norm_commutes_with_the_split_permutation():
+    # permuting the weights together with the channels (the pages' split-RoPE
+    # load step) leaves the normalised values permuted the same way
+    r = rng(21)
+    x, w = r.standard_normal((4, 128)), r.standard_normal(128)
+    P = oracle.interleaved_to_split_permutation(128)
+    assert np.allclose(oracle.rms_norm(x[:, P], w[P], 1e-6), oracle.rms_norm(x, w, 1e-6)[:, P], rtol=0, atol=1e-14)
+
+
+def test_rms_norm_then_rope_keeps_unit_rms():
+    r = rng(22)
+    x = r.standard_normal((6, 64)) * 3.0
+    cos, sin = oracle.rope_tables(np.arange(6)[:, None] * 5, (64,), 10000.0)
+    y = oracle.rope_split_halves(oracle.rms_norm(x, np.ones(64), 0.0), cos, sin)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=0, atol=1e-13)
+
+
+def test_negative_control_sum_instead_of_mean_fails_unit_rms():
+    x = rng(23).standard_normal((2, 64))
+    wrong = x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    assert not np.allclose(np.mean(wrong * wrong, axis=-1), 1.0, atol=1e-3)
+
+
 # ------------------------------------------------------------------ attention
 def rand_qkv(seed, B, H, Sq, Skv, d, scale=1.0):
     r = rng(seed)
