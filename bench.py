@@ -214,6 +214,14 @@ def config_table(np, torch, ops, W, dev, n_iter):
                                                  rope_q=tabs, rope_k=tabs, out=o, lse=lse,
                                                  workspace=ws), n)
         ent = {"us": us, "tflops": w.valid_flop / us / 1e6, "pct_peak": w.valid_flop / us / 1e6 / PEAK_BF16_TFLOPS * 100}
+        if name == "wan480":   # the same call with the per-head q/k RMSNorm fused into the pre-pass
+            wn = torch.ones(w.d, dtype=torch.float32, device=dev)
+            wsn = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
+                                                          rope_q=tabs, rope_k=tabs, q_norm=wn, k_norm=wn), 256),
+                              dtype=torch.uint8, device=dev)
+            ent["with_qk_rmsnorm_us"] = time_us(torch, lambda: ops.attn_fwd(
+                qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=tabs, rope_k=tabs, out=o, lse=lse,
+                workspace=wsn, q_norm=wn, k_norm=wn), n)
         if w.kv_valid:   # short-KV: report the HBM side too (Q, K, V, O, LSE once each)
             nbytes = w.B * w.H * (2 * w.s_pad * w.d * 2 + 2 * w.k_pad * w.d * 2 + w.s_pad * 4)
             ent.update({"hbm_bytes": nbytes, "hbm_GBps": nbytes / us / 1e3})

@@ -98,8 +98,9 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * result that dit_lse_merge will combine), written for rows [0, s_q).
  * lse: fp32 dense [B, H, s_q], natural log, or NULL to skip it.
  *
- * workspace: device scratch for the once-per-call rotated copies of K and Q
- * (dense bf16 [B, H, s, d] each, when their tables are given) and, under the
+ * workspace: device scratch for the once-per-call rotated (and normalised)
+ * copies of K and Q (dense bf16 [B, H, s, d] each, when their tables or norm
+ * weights are given) and, under the
  * BALANCED schedule, the partial results of split query tiles and their
  * arrival counters. Required (non-NULL, 256-byte aligned, at least
  * dit_attn_workspace_size() bytes) when that size is non-zero. The caller
@@ -107,6 +108,16 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * workspace must not overlap.
  *
  * schedule: a dit_schedule value (0 = AUTO).
+ *
+ * q/k RMS normalisation (optional, fused into the rotation pre-pass; the
+ * per-head q/k RMSNorm that precedes RoPE in FLUX and Wan, Difflet PR #153
+ * split-RoPE commits): with q_norm_w (k_norm_w) non-NULL, each head vector
+ * of Q (K) is first replaced by
+ *   y_c = x_c / sqrt(mean_c' x_c'^2 + norm_eps) * w_c
+ * in fp32 from the bf16 input, then rotated (when its tables are given) and
+ * rounded once to bf16. w: device fp32 [d] in the channel order of Q/K (the
+ * split-halves order: permute it with the channels), 16-byte aligned.
+ * norm_eps must be finite and >= 0 (0 with an all-zero row gives NaN there).
  */
 typedef struct dit_attn_desc {
   int32_t B, H, d;               /* d in {64, 128}, else DIT_ERR_UNSUPPORTED */
@@ -123,6 +134,8 @@ typedef struct dit_attn_desc {
   void *workspace;
   size_t workspace_bytes;
   int32_t schedule;              /* dit_schedule */
+  const float *q_norm_w, *k_norm_w;  /* fp32 [d] RMSNorm weights or NULL (no norm) */
+  float norm_eps;
 } dit_attn_desc;
 
 /* Bytes of workspace dit_attn_fwd needs for `desc` (0 when K is not rotated

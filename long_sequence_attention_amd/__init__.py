@@ -53,7 +53,8 @@ def plan_padding(s_valid: int, multiple: int) -> int:
     return out.value
 
 
-def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule=0):
+def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule=0,
+               q_norm=None, k_norm=None, norm_eps=1e-6):
     B, H, s_q, d = q.shape
     desc = N.AttnDesc()
     desc.B, desc.H, desc.d = B, H, d
@@ -70,14 +71,20 @@ def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, sch
     if rope_k is not None:
         desc.cos_k, desc.sin_k = rope_k[0].data_ptr(), rope_k[1].data_ptr()
     desc.schedule = int(schedule)
+    if q_norm is not None:
+        desc.q_norm_w = q_norm.data_ptr()
+    if k_norm is not None:
+        desc.k_norm_w = k_norm.data_ptr()
+    desc.norm_eps = float(norm_eps)
     return desc
 
 
-def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, schedule=0) -> int:
+def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, schedule=0,
+                        q_norm=None, k_norm=None) -> int:
     """Workspace bytes attn_fwd needs (dit_attn_workspace_size) on q's device."""
     q_valid = q.shape[2] if q_valid is None else int(q_valid)
     kv_valid = k.shape[2] if kv_valid is None else int(kv_valid)
-    desc = _attn_desc(q, k, v, q, None, q_valid, kv_valid, rope_q, rope_k, 0.0, schedule)
+    desc = _attn_desc(q, k, v, q, None, q_valid, kv_valid, rope_q, rope_k, 0.0, schedule, q_norm, k_norm)
     need = ctypes.c_size_t()
     with torch.cuda.device(q.device):
         N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_workspace_size")
@@ -85,13 +92,16 @@ def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, ro
 
 
 def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
-             out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None, schedule=0):
+             out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None, schedule=0,
+             q_norm=None, k_norm=None, norm_eps=1e-6):
     """Attention forward (dit_attn_fwd).
 
     q: [B, H, s_q, d], k/v: [B, H, s_kv, d] bf16 device tensors, any strides
     with d contiguous (e.g. a permuted [B, S, H, d] buffer). Rows >= q_valid /
     kv_valid are tail pads. rope_q / rope_k: (cos, sin) fp32 [S, d/2] tables
     or None. schedule: 0 auto, 1 one workgroup per query tile, 2 balanced.
+    q_norm / k_norm: fp32 [d] RMSNorm weights (per-head q/k RMS normalisation
+    before RoPE, epsilon norm_eps) or None.
     Returns (O, LSE) with O [B, H, s_q, d] in out_dtype (or `out`) and LSE
     fp32 [B, H, s_q] (natural log), or O alone if return_lse=False.
     """
@@ -120,7 +130,13 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
         _need_cuda("lse", lse, torch.float32)
         if lse.shape != (B, H, s_q) or not lse.is_contiguous():
             raise ValueError("lse must be contiguous fp32 [B, H, s_q]")
-    desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule)
+    for name, wt in (("q_norm", q_norm), ("k_norm", k_norm)):
+        if wt is not None:
+            _need_cuda(name, wt, torch.float32)
+            if wt.shape != (d,) or not wt.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous fp32 [{d}] tensor")
+    desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule, q_norm, k_norm,
+                      norm_eps)
     need = ctypes.c_size_t()
     with torch.cuda.device(q.device):
         N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")

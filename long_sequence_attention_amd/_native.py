@@ -50,6 +50,8 @@ class AttnDesc(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("schedule", ctypes.c_int32),
+        ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
     ]
 
 

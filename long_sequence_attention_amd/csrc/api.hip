@@ -78,9 +78,13 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   if (!std::isfinite(scale) || scale < 0.0f) return fail(DIT_ERR_INVALID, "sm_scale=%g must be finite and positive", (double)d->sm_scale);
   const int64_t nq = ((int64_t)d->s_q + dit::kAttnBlockM - 1) / dit::kAttnBlockM;
   if (nq * d->H * d->B > 0x7fffffffLL) return fail(DIT_ERR_UNSUPPORTED, "too many query tiles for one launch");
-  if ((d->cos_q != nullptr || d->cos_k != nullptr) && (int64_t)d->B * d->H > 4LL * 65535)
-    return fail(DIT_ERR_UNSUPPORTED, "rotation needs B * H <= 262140 (one grid plane per four heads)");
-  const void *ptrs[] = {d->q, d->k, d->v, d->o, d->cos_q, d->sin_q, d->cos_k, d->sin_k};
+  const bool prep_q = d->cos_q != nullptr || d->q_norm_w != nullptr;
+  const bool prep_k = d->cos_k != nullptr || d->k_norm_w != nullptr;
+  if ((d->q_norm_w != nullptr || d->k_norm_w != nullptr) && (!std::isfinite(d->norm_eps) || d->norm_eps < 0.0f))
+    return fail(DIT_ERR_INVALID, "norm_eps=%g must be finite and >= 0", (double)d->norm_eps);
+  if ((prep_q || prep_k) && (int64_t)d->B * d->H > 4LL * 65535)
+    return fail(DIT_ERR_UNSUPPORTED, "rotation / normalisation needs B * H <= 262140 (one grid plane per four heads)");
+  const void *ptrs[] = {d->q, d->k, d->v, d->o, d->cos_q, d->sin_q, d->cos_k, d->sin_k, d->q_norm_w, d->k_norm_w};
   for (const void *p : ptrs)
     if (p != nullptr && !aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
   if (d->lse != nullptr && (reinterpret_cast<uintptr_t>(d->lse) & 3u)) return fail(DIT_ERR_INVALID, "lse must be 4-byte aligned");
@@ -104,11 +108,11 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   return DIT_OK;
 }
 
-// Launch plan of one dit_attn_fwd call: Q / K rotation and schedule, and where
+// Launch plan of one dit_attn_fwd call: Q / K pre-pass and schedule, and where
 // their scratch lives inside the caller's workspace.
 struct AttnPlan {
-  size_t k_bytes = 0;       // rotated K, dense [B, H, s_kv, d] bf16
-  size_t q_bytes = 0;       // rotated Q, dense [B, H, s_q, d] bf16 (after K)
+  size_t k_bytes = 0;       // prepared (normalised / rotated) K, dense [B, H, s_kv, d] bf16
+  size_t q_bytes = 0;       // prepared Q, dense [B, H, s_q, d] bf16 (after K)
   int splits = 1;           // key-split pieces per q-tile (1 = one workgroup per q-tile)
   size_t part_o_off = 0, part_l_off = 0, count_off = 0;
   int64_t n_counts = 0;
@@ -129,8 +133,10 @@ double split_cost(int64_t nq, int64_t nk, int64_t S, int64_t slots) {
 
 int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   AttnPlan p;
-  if (d->cos_k != nullptr && d->kv_valid > 0) p.k_bytes = round_up((size_t)d->B * d->H * (size_t)d->s_kv * d->d * 2, 256);
-  if (d->cos_q != nullptr && d->kv_valid > 0) p.q_bytes = round_up((size_t)d->B * d->H * (size_t)d->s_q * d->d * 2, 256);
+  if ((d->cos_k != nullptr || d->k_norm_w != nullptr) && d->kv_valid > 0)
+    p.k_bytes = round_up((size_t)d->B * d->H * (size_t)d->s_kv * d->d * 2, 256);
+  if ((d->cos_q != nullptr || d->q_norm_w != nullptr) && d->kv_valid > 0)
+    p.q_bytes = round_up((size_t)d->B * d->H * (size_t)d->s_q * d->d * 2, 256);
   const int64_t nq = (int64_t)d->B * d->H * ((d->s_q + kBlockM - 1) / kBlockM);
   const int64_t nk = (d->kv_valid + kBlockN - 1) / kBlockN;
   if (d->schedule < DIT_SCHED_AUTO || d->schedule > DIT_SCHED_BALANCED)
@@ -237,15 +243,17 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
   p.n_qtiles = (d.s_q + dit::kAttnBlockM - 1) / dit::kAttnBlockM;
   p.scale_log2 = scale * 1.4426950408889634f;
 
-  // one pre-pass rotates K (valid rows) and Q (all rows) into the workspace
+  // one pre-pass normalises and / or rotates K (valid rows) and Q (all rows)
+  // into the workspace
   if (pl.k_bytes + pl.q_bytes > 0) {
     dit::RopeRotateParams r{};
     char *ws = static_cast<char *>(d.workspace);
     r.B = d.B; r.H = d.H; r.d = d.d;
+    r.eps = d.norm_eps;
     if (pl.k_bytes > 0) {
       dit::RopeSeg &g = r.seg[r.n_seg++];
       g.x = p.k; g.y = reinterpret_cast<dit::bf16_t *>(ws);
-      g.cos_t = d.cos_k; g.sin_t = d.sin_k;
+      g.cos_t = d.cos_k; g.sin_t = d.sin_k; g.norm_w = d.k_norm_w;
       g.xs_b = p.ks_b; g.xs_h = p.ks_h; g.xs_s = p.ks_s;
       g.S = d.s_kv; g.rows = d.kv_valid;
       p.k = g.y;
@@ -254,7 +262,7 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
     if (pl.q_bytes > 0) {
       dit::RopeSeg &g = r.seg[r.n_seg++];
       g.x = p.q; g.y = reinterpret_cast<dit::bf16_t *>(ws + pl.k_bytes);
-      g.cos_t = d.cos_q; g.sin_t = d.sin_q;
+      g.cos_t = d.cos_q; g.sin_t = d.sin_q; g.norm_w = d.q_norm_w;
       g.xs_b = p.qs_b; g.xs_h = p.qs_h; g.xs_s = p.qs_s;
       g.S = d.s_q; g.rows = d.s_q;
       p.q = g.y;

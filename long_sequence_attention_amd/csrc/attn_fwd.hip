@@ -1,6 +1,7 @@
 // Attention forward for gfx950: bf16 MFMA (v_mfma_f32_32x32x16_bf16) with
 // fp32 accumulation, online softmax in exp2 form, exact tail-pad masking,
-// and a split-halves RoPE pre-pass that rotates Q and K once per call.
+// and a pre-pass that applies the optional per-head q/k RMS normalisation and
+// the split-halves RoPE to Q and K once per call.
 //
 // What is computed (the pages' problem statement): for each (b, h) and query
 // row i < q_valid, O_i = sum_{j < kv_valid} softmax_j(scale * q'_i . k'_j) v_j
@@ -62,22 +63,28 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 __device__ __forceinline__ u32x4 ldg16(const bf16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// Split-halves rotation of 8 channel pairs (lo holds channels i..i+7 of the
-// first half, hi the partners d/2 later) in fp32, rounded once to bf16.
-__device__ __forceinline__ void rotate8(u32x4 &lo, u32x4 &hi, const float *cv, const float *sv) {
-  u32x4 nlo, nhi;
+// Split-halves rotation of 8 channel pairs in fp32: x1 holds channels
+// i..i+7 of the first half, x2 the partners d/2 later.
+__device__ __forceinline__ void rotate8(float *x1, float *x2, const float *cv, const float *sv) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y1 = fmaf(x1[e], cv[e], -x2[e] * sv[e]);
+    const float y2 = fmaf(x2[e], cv[e], x1[e] * sv[e]);
+    x1[e] = y1;
+    x2[e] = y2;
+  }
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 &v, float *x) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float x1a = bf16_lo(lo[w]), x1b = bf16_hi(lo[w]);
-    const float x2a = bf16_lo(hi[w]), x2b = bf16_hi(hi[w]);
-    const float ca = cv[2 * w], cb = cv[2 * w + 1], sa = sv[2 * w], sb = sv[2 * w + 1];
-    const float y1a = fmaf(x1a, ca, -x2a * sa), y1b = fmaf(x1b, cb, -x2b * sb);
-    const float y2a = fmaf(x2a, ca, x1a * sa), y2b = fmaf(x2b, cb, x1b * sb);
-    nlo[w] = pack_bf16x2(y1a, y1b);
-    nhi[w] = pack_bf16x2(y2a, y2b);
+    x[2 * w] = bf16_lo(v[w]);
+    x[2 * w + 1] = bf16_hi(v[w]);
   }
-  lo = nlo;
-  hi = nhi;
+}
+
+__device__ __forceinline__ u32x4 pack8(const float *x) {
+  return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
 }
 
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
@@ -589,12 +596,14 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   if (last_flag) merge_pieces<D>(p, ln, T, s, b, h, qrow, row_ok, acc_o, lse2);
 }
 
-// Rotation pre-pass of Q and K (blockIdx.y picks the tensor). A thread owns
-// one 8-channel run of the first half of a row and its partner run d/2
-// later: it loads that row's 16 table values once and applies them to the
-// row of up to kRopeHeads (b, h) pairs (blockIdx.z picks the group), so the
-// tables are read once per row and head group rather than once per head.
-// RUNS = d/16 threads per row, 256/RUNS rows per block iteration.
+// Pre-pass of Q and K (blockIdx.y picks the tensor): optional per-head RMS
+// normalisation with weights, then optional split-halves rotation, in fp32
+// from the bf16 input, rounded once to bf16. A thread owns one 8-channel run
+// of the first half of a row and its partner run d/2 later: it loads that
+// row's 16 table values once and applies them to the row of up to
+// kRopeHeads (b, h) pairs (blockIdx.z picks the group), so the tables are
+// read once per row and head group rather than once per head. The RMS of a
+// head vector is summed over the RUNS = d/16 consecutive lanes of its row.
 constexpr int kRopeHeads = 4;
 
 template <int RUNS>
@@ -605,10 +614,21 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
   const int nbh = p.B * p.H;
   const int bh0 = blockIdx.z * kRopeHeads;
   const int nh = nbh - bh0 < kRopeHeads ? nbh - bh0 : kRopeHeads;
+  const bool rot = g.cos_t != nullptr, nrm = g.norm_w != nullptr;
+  float w1[8], w2[8];
+  if (nrm) {
+    const float4 a0 = *reinterpret_cast<const float4 *>(g.norm_w + c * 8);
+    const float4 a1 = *reinterpret_cast<const float4 *>(g.norm_w + c * 8 + 4);
+    const float4 b0 = *reinterpret_cast<const float4 *>(g.norm_w + HALF + c * 8);
+    const float4 b1 = *reinterpret_cast<const float4 *>(g.norm_w + HALF + c * 8 + 4);
+    w1[0] = a0.x; w1[1] = a0.y; w1[2] = a0.z; w1[3] = a0.w; w1[4] = a1.x; w1[5] = a1.y; w1[6] = a1.z; w1[7] = a1.w;
+    w2[0] = b0.x; w2[1] = b0.y; w2[2] = b0.z; w2[3] = b0.w; w2[4] = b1.x; w2[5] = b1.y; w2[6] = b1.z; w2[7] = b1.w;
+  }
+  const float inv_d = 1.0f / (float)(2 * HALF);
   for (int s = blockIdx.x * ROWS + threadIdx.x / RUNS; s < g.rows; s += gridDim.x * ROWS) {
-    const int64_t to = (int64_t)s * HALF + c * 8;
     float cv[8], sv[8];
-    {
+    if (rot) {
+      const int64_t to = (int64_t)s * HALF + c * 8;
       const float4 c0 = *reinterpret_cast<const float4 *>(g.cos_t + to);
       const float4 c1 = *reinterpret_cast<const float4 *>(g.cos_t + to + 4);
       const float4 s0 = *reinterpret_cast<const float4 *>(g.sin_t + to);
@@ -616,7 +636,7 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
       cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w; cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
       sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
     }
-    // all loads of the group first, then the rotations and stores
+    // all loads of the group first, then the arithmetic and stores
     u32x4 lo[kRopeHeads], hi[kRopeHeads];
 #pragma unroll
     for (int j = 0; j < kRopeHeads; ++j) {
@@ -630,10 +650,26 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
 #pragma unroll
     for (int j = 0; j < kRopeHeads; ++j) {
       if (j < nh) {
-        rotate8(lo[j], hi[j], cv, sv);
+        float x1[8], x2[8];
+        unpack8(lo[j], x1);
+        unpack8(hi[j], x2);
+        if (nrm) {
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(x1[e], x1[e], fmaf(x2[e], x2[e], ss));
+#pragma unroll
+          for (int m = 1; m < RUNS; m <<= 1) ss += __shfl_xor(ss, m);
+          const float inv = 1.0f / sqrtf(fmaf(ss, inv_d, p.eps));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x1[e] = x1[e] * inv * w1[e];
+            x2[e] = x2[e] * inv * w2[e];
+          }
+        }
+        if (rot) rotate8(x1, x2, cv, sv);
         bf16_t *yr = g.y + ((int64_t)(bh0 + j) * g.S + s) * (2 * HALF);
-        *reinterpret_cast<u32x4 *>(yr + c * 8) = lo[j];
-        *reinterpret_cast<u32x4 *>(yr + HALF + c * 8) = hi[j];
+        *reinterpret_cast<u32x4 *>(yr + c * 8) = pack8(x1);
+        *reinterpret_cast<u32x4 *>(yr + HALF + c * 8) = pack8(x2);
       }
     }
   }

@@ -56,21 +56,24 @@ struct AttnParams {
   int32_t *sk_count; // [q-tiles] arrival counters, zero on entry (left zero on exit)
 };
 
-// One tensor of the rotation pre-pass: rows [0, rows) of x ((b, h, s)
-// strides in elements) rotated into the dense [B, H, S, d] buffer y with the
-// fp32 [>= rows, d/2] tables cos_t / sin_t.
+// One tensor of the pre-pass: rows [0, rows) of x ((b, h, s) strides in
+// elements) RMS-normalised with the fp32 [d] weights norm_w (when non-NULL),
+// rotated with the fp32 [>= rows, d/2] tables cos_t / sin_t (when non-NULL)
+// and written to the dense [B, H, S, d] buffer y.
 struct RopeSeg {
   const bf16_t *x;
   bf16_t *y;
   const float *cos_t, *sin_t;
+  const float *norm_w;
   int64_t xs_b, xs_h, xs_s;
   int32_t S, rows;
 };
 
-// Parameters of the Q / K rotation pre-pass (one launch for both tensors).
+// Parameters of the Q / K pre-pass (one launch for both tensors).
 struct RopeRotateParams {
   RopeSeg seg[2];
   int32_t n_seg, B, H, d;
+  float eps;   // RMSNorm epsilon
 };
 
 constexpr int kMaxMergeParts = 16;

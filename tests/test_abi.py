@@ -73,6 +73,9 @@ def _desc(**kw):
     (dict(cos_q=0x20000000), -1, b"cos_q and sin_q"),
     (dict(sin_k=0x20000000), -1, b"cos_k and sin_k"),
     (dict(q=0x10000008), -2, b"16-byte aligned"),
+    (dict(q_norm_w=0x20000000, norm_eps=-1.0), -1, b"norm_eps"),
+    (dict(k_norm_w=0x20000000, norm_eps=float("inf")), -1, b"norm_eps"),
+    (dict(k_norm_w=0x20000004, norm_eps=1e-6), -2, b"16-byte aligned"),
 ])
 def test_attn_fwd_rejects_bad_arguments_before_any_hip_call(L, kw, code, msg):
     d = _desc(**kw)
@@ -93,6 +96,11 @@ def test_attn_fwd_rejects_bad_strides_and_missing_workspace(L):
     assert size.value == 1 * 2 * 256 * 128 * 2
     d = _desc()
     assert L.dit_attn_workspace_size(ctypes.byref(d), ctypes.byref(size)) == 0 and size.value == 0
+    # norm weights alone also need the prepared copy (Q after K, 256-byte aligned)
+    d = _desc(q_norm_w=0x20000000, k_norm_w=0x20000000, norm_eps=1e-6)
+    assert L.dit_attn_workspace_size(ctypes.byref(d), ctypes.byref(size)) == 0
+    assert size.value == 2 * (1 * 2 * 256 * 128 * 2)
+    assert L.dit_attn_fwd(ctypes.byref(d), None) == -1 and b"workspace" in L.dit_last_error()
     assert L.dit_attn_fwd(None, None) == -1
 
 
