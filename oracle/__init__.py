@@ -24,6 +24,11 @@ What each function follows (pages are cited by title and section):
     exactly (Difflet PR #153, Wan padding commit; maxdiffusion PR #491, the
     ragged KV tail carries the real length). Pad query rows give O = 0 and
     LSE = -inf (a convention: -inf is the merge's identity).
+  * segment_valid_rows / attention_segmented -- sequences cut into segments
+    that are each padded at their own tail (maxdiffusion PR #491: lane
+    padding per ring segment on the Ulysses-ring path; the padding
+    descriptor carries the real length and the segment count), attended as
+    one softmax over every real key.
   * lse_merge -- combining per-key-shard (O, LSE) pairs into the single-pass
     result (mstar PR #376, attention_over_sharded_keys).
   * pad_tokens / unpad_tokens / plan_padding -- tail padding of token rows to
@@ -45,6 +50,8 @@ from .reference import (  # noqa: F401
     rms_norm,
     attention,
     attention_bruteforce,
+    segment_valid_rows,
+    attention_segmented,
     lse_merge,
     dit_path,
 )

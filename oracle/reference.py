@@ -164,6 +164,41 @@ def attention(q, k, v, q_valid: int, kv_valid: int, scale: float | None = None,
     return O, L
 
 
+def segment_valid_rows(S: int, seg_len: int, valid: int) -> np.ndarray:
+    """Indices of the real rows of a sequence of S rows cut into segments of
+    seg_len rows, each holding `valid` real rows followed by its own tail
+    pad (maxdiffusion PR #491: on the Ulysses-ring path each ring segment is
+    padded at its own tail)."""
+    if seg_len <= 0 or S % seg_len:
+        raise ValueError("S must be a positive multiple of seg_len")
+    r = np.arange(S)
+    return r[(r % seg_len) < valid]
+
+
+def attention_segmented(q, k, v, q_seg_len: int, q_valid: int, kv_seg_len: int, kv_valid: int,
+                        scale: float | None = None):
+    """Attention over tail-padded segments, float64: query row i is real when
+    i mod q_seg_len < q_valid, key j when j mod kv_seg_len < kv_valid; every
+    real query attends to every real key of every segment (one softmax over
+    their union). Pad query rows give O = 0 and LSE = -inf.
+
+    Written as the plain definition: the real keys are gathered into one
+    contiguous block and `attention` runs on it for the real query rows.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, S_q, d = q.shape
+    qr = segment_valid_rows(S_q, q_seg_len, q_valid)
+    kr = segment_valid_rows(np.asarray(k).shape[2], kv_seg_len, kv_valid)
+    kc = np.asarray(k, dtype=np.float64)[:, :, kr]
+    vc = np.asarray(v, dtype=np.float64)[:, :, kr]
+    Oc, Lc = attention(q[:, :, qr], kc, vc, len(qr), len(kr), scale)
+    O = np.zeros((B, H, S_q, d))
+    L = np.full((B, H, S_q), -np.inf)
+    O[:, :, qr] = Oc
+    L[:, :, qr] = Lc
+    return O, L
+
+
 def attention_bruteforce(q, k, v, q_valid: int, kv_valid: int, scale: float | None = None):
     """The same definition as `attention`, in pure-Python loops (tiny sizes)."""
     q = np.asarray(q, dtype=np.float64)

@@ -320,6 +320,52 @@ def test_row_subset_matches_full_evaluation():
     assert np.allclose(Lr[f], Lf[:, :, rows][f], rtol=0, atol=1e-13)
 
 
+# ------------------------------------------------------------------ segmented
+def test_segment_rows_worked_example():
+    # 3 segments of 4 rows, 3 real each: rows 3, 7, 11 are the tail pads
+    assert oracle.segment_valid_rows(12, 4, 3).tolist() == [0, 1, 2, 4, 5, 6, 8, 9, 10]
+    assert oracle.segment_valid_rows(12, 12, 12).tolist() == list(range(12))
+
+
+def test_segmented_with_one_segment_is_plain_attention():
+    r = rng(30)
+    q, k, v = (r.standard_normal((1, 2, 40, 16)) for _ in range(3))
+    O1, L1 = oracle.attention_segmented(q, k, v, 40, 37, 40, 33)
+    O2, L2 = oracle.attention(q, k, v, 37, 33)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_segmented_equals_merge_of_per_segment_attention():
+    # one softmax over all real keys = lse_merge of each segment's own result
+    r = rng(31)
+    q = r.standard_normal((1, 2, 30, 16))
+    k, v = r.standard_normal((1, 2, 48, 16)), r.standard_normal((1, 2, 48, 16))
+    O, L = oracle.attention_segmented(q, k, v, 30, 30, 16, 13)
+    parts = [oracle.attention(q, k[:, :, 16 * i:16 * (i + 1)], v[:, :, 16 * i:16 * (i + 1)], 30, 13)
+             for i in range(3)]
+    Om, Lm = oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+    assert np.allclose(O, Om, rtol=0, atol=1e-12) and np.allclose(L, Lm, rtol=0, atol=1e-12)
+
+
+def test_segmented_pads_and_segment_order_do_not_matter():
+    r = rng(32)
+    q = r.standard_normal((1, 1, 20, 8))
+    k, v = r.standard_normal((1, 1, 30, 8)), r.standard_normal((1, 1, 30, 8))
+    O, L = oracle.attention_segmented(q, k, v, 10, 7, 10, 6)
+    pad = np.ones(30, bool)
+    pad[oracle.segment_valid_rows(30, 10, 6)] = False
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, pad] = 1e30
+    v2[:, :, pad] = -1e30
+    O2, L2 = oracle.attention_segmented(q, k2, v2, 10, 7, 10, 6)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+    perm = np.r_[20:30, 0:10, 10:20]
+    O3, L3 = oracle.attention_segmented(q, k[:, :, perm], v[:, :, perm], 10, 7, 10, 6)
+    assert np.allclose(O, O3, rtol=0, atol=1e-12) and np.allclose(L, L3, rtol=0, atol=1e-12)
+    qpad = ~np.isin(np.arange(20), oracle.segment_valid_rows(20, 10, 7))
+    assert (O[:, :, qpad] == 0).all() and np.isneginf(L[:, :, qpad]).all()
+
+
 # ------------------------------------------------------------------ merge
 def _shards(q, k, v, cuts, q_valid, total_valid):
     parts = []
