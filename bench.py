@@ -222,6 +222,25 @@ def config_table(np, torch, ops, W, dev, n_iter):
             ent["with_qk_rmsnorm_us"] = time_us(torch, lambda: ops.attn_fwd(
                 qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=tabs, rope_k=tabs, out=o, lse=lse,
                 workspace=wsn, q_norm=wn, k_norm=wn), n)
+        if name == "wan480":   # the ring layout: two segments of 2340 real rows, each padded to 2368
+            per, L = w.s_valid // 2, 2368
+            qs, ks, vs = (torch.zeros((w.B, w.H, 2 * L, w.d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+            for src, dst in ((qd, qs), (kd, ks), (vd, vs)):
+                for i in range(2):
+                    dst[:, :, i * L:i * L + per] = src[:, :, i * per:(i + 1) * per]
+            cs2, sn2 = (torch.zeros((2 * L, w.d // 2), dtype=torch.float32, device=dev) for _ in range(2))
+            for i in range(2):
+                cs2[i * L:i * L + per] = cos[i * per:(i + 1) * per]
+                sn2[i * L:i * L + per] = sin[i * per:(i + 1) * per]
+            os2 = torch.empty_like(qs)
+            ls2 = torch.empty((w.B, w.H, 2 * L), dtype=torch.float32, device=dev)
+            wss = torch.empty(max(ops.attn_workspace_size(qs, ks, vs, q_valid=per, kv_valid=per, q_seg_len=L,
+                                                          kv_seg_len=L, rope_q=(cs2, sn2), rope_k=(cs2, sn2)), 256),
+                              dtype=torch.uint8, device=dev)
+            ent["ring_2_segments_us"] = time_us(torch, lambda: ops.attn_fwd(
+                qs, ks, vs, q_valid=per, kv_valid=per, q_seg_len=L, kv_seg_len=L, rope_q=(cs2, sn2),
+                rope_k=(cs2, sn2), out=os2, lse=ls2, workspace=wss), n)
+            del qs, ks, vs, os2, wss
         if w.kv_valid:   # short-KV: report the HBM side too (Q, K, V, O, LSE once each)
             nbytes = w.B * w.H * (2 * w.s_pad * w.d * 2 + 2 * w.k_pad * w.d * 2 + w.s_pad * 4)
             ent.update({"hbm_bytes": nbytes, "hbm_GBps": nbytes / us / 1e3})

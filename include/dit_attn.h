@@ -118,6 +118,16 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * rounded once to bf16. w: device fp32 [d] in the channel order of Q/K (the
  * split-halves order: permute it with the channels), 16-byte aligned.
  * norm_eps must be finite and >= 0 (0 with an all-zero row gives NaN there).
+ *
+ * Segments (the ring layout: maxdiffusion PR #491 pads each ring segment at
+ * its own tail): with kv_seg_len > 0, K/V hold s_kv / kv_seg_len segments of
+ * kv_seg_len rows and kv_valid counts the real rows at the head of EACH
+ * segment; key j is real iff j mod kv_seg_len < kv_valid. Likewise
+ * q_seg_len > 0 makes query row i real iff i mod q_seg_len < q_valid. One
+ * softmax runs over all real keys of all segments; pad query rows get O = +0
+ * and LSE = -inf. s must be a multiple of its segment length and valid <=
+ * segment length (else DIT_ERR_INVALID); kv_seg_len must be a multiple of 64
+ * and the schedule not BALANCED (else DIT_ERR_UNSUPPORTED).
  */
 typedef struct dit_attn_desc {
   int32_t B, H, d;               /* d in {64, 128}, else DIT_ERR_UNSUPPORTED */
@@ -136,6 +146,7 @@ typedef struct dit_attn_desc {
   int32_t schedule;              /* dit_schedule */
   const float *q_norm_w, *k_norm_w;  /* fp32 [d] RMSNorm weights or NULL (no norm) */
   float norm_eps;
+  int32_t q_seg_len, kv_seg_len; /* 0, or segment length: see "Segments" above */
 } dit_attn_desc;
 
 /* Bytes of workspace dit_attn_fwd needs for `desc` (0 when K is not rotated

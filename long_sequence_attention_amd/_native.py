@@ -52,6 +52,7 @@ class AttnDesc(ctypes.Structure):
         ("schedule", ctypes.c_int32),
         ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p),
         ("norm_eps", ctypes.c_float),
+        ("q_seg_len", ctypes.c_int32), ("kv_seg_len", ctypes.c_int32),
     ]
 
 

@@ -63,10 +63,22 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   if (d->d <= 0 || (d->d % 2) != 0) return fail(DIT_ERR_INVALID, "head dim d=%d must be positive and even", d->d);
   if (d->d != 64 && d->d != 128) return fail(DIT_ERR_UNSUPPORTED, "head dim d=%d: kernels exist for d in {64, 128}", d->d);
   if (d->s_q < 0 || d->s_kv < 0) return fail(DIT_ERR_INVALID, "s_q and s_kv must be >= 0");
-  if (d->q_valid < 0 || d->q_valid > d->s_q)
-    return fail(DIT_ERR_INVALID, "q_valid=%d must lie in [0, s_q=%d]", d->q_valid, d->s_q);
-  if (d->kv_valid < 0 || d->kv_valid > d->s_kv)
-    return fail(DIT_ERR_INVALID, "kv_valid=%d must lie in [0, s_kv=%d]", d->kv_valid, d->s_kv);
+  if (d->q_seg_len < 0 || d->kv_seg_len < 0) return fail(DIT_ERR_INVALID, "segment lengths must be >= 0");
+  if (d->q_seg_len > 0 && d->s_q % d->q_seg_len != 0)
+    return fail(DIT_ERR_INVALID, "s_q=%d is not a multiple of q_seg_len=%d", d->s_q, d->q_seg_len);
+  if (d->kv_seg_len > 0 && d->s_kv % d->kv_seg_len != 0)
+    return fail(DIT_ERR_INVALID, "s_kv=%d is not a multiple of kv_seg_len=%d", d->s_kv, d->kv_seg_len);
+  const int q_lim = d->q_seg_len > 0 ? d->q_seg_len : d->s_q;
+  const int kv_lim = d->kv_seg_len > 0 ? d->kv_seg_len : d->s_kv;
+  if (d->q_valid < 0 || d->q_valid > q_lim)
+    return fail(DIT_ERR_INVALID, "q_valid=%d must lie in [0, %d] (s_q or q_seg_len)", d->q_valid, q_lim);
+  if (d->kv_valid < 0 || d->kv_valid > kv_lim)
+    return fail(DIT_ERR_INVALID, "kv_valid=%d must lie in [0, %d] (s_kv or kv_seg_len)", d->kv_valid, kv_lim);
+  if (d->kv_seg_len > 0 && d->kv_seg_len % dit::kAttnBlockN != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "kv_seg_len=%d must be a multiple of the %d-row key tile", d->kv_seg_len,
+                dit::kAttnBlockN);
+  if (d->kv_seg_len > 0 && d->schedule == DIT_SCHED_BALANCED)
+    return fail(DIT_ERR_UNSUPPORTED, "the balanced schedule does not cover key segments");
   if (d->o_dtype != DIT_BF16 && d->o_dtype != DIT_F32) return fail(DIT_ERR_INVALID, "o_dtype=%d is not a dit_dtype", d->o_dtype);
   if (d->s_q > 0 && (d->q == nullptr || d->o == nullptr)) return fail(DIT_ERR_INVALID, "q and o must be non-NULL when s_q > 0");
   if (d->kv_valid > 0 && (d->k == nullptr || d->v == nullptr))
@@ -239,6 +251,9 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
   p.lse = d.lse;
   p.B = d.B; p.H = d.H; p.s_q = d.s_q; p.s_kv = d.s_kv;
   p.q_valid = d.q_valid; p.kv_valid = d.kv_valid;
+  p.q_seg_len = d.q_seg_len;
+  p.kv_seg_len = d.kv_seg_len;
+  p.n_kv_seg = d.kv_seg_len > 0 ? d.s_kv / d.kv_seg_len : 1;
   p.o_f32 = d.o_dtype == DIT_F32;
   p.n_qtiles = (d.s_q + dit::kAttnBlockM - 1) / dit::kAttnBlockM;
   p.scale_log2 = scale * 1.4426950408889634f;
@@ -255,7 +270,7 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
       g.x = p.k; g.y = reinterpret_cast<dit::bf16_t *>(ws);
       g.cos_t = d.cos_k; g.sin_t = d.sin_k; g.norm_w = d.k_norm_w;
       g.xs_b = p.ks_b; g.xs_h = p.ks_h; g.xs_s = p.ks_s;
-      g.S = d.s_kv; g.rows = d.kv_valid;
+      g.S = d.s_kv; g.rows = d.kv_seg_len > 0 ? d.s_kv : d.kv_valid;   // segments: every segment's real rows
       p.k = g.y;
       p.ks_b = (int64_t)d.H * d.s_kv * d.d; p.ks_h = (int64_t)d.s_kv * d.d; p.ks_s = d.d;
     }

@@ -308,51 +308,74 @@ struct Lane {
   int kx, vx;   // operand read offsets of d-chunk 0 (see the kernel prologue)
 };
 
-// Attention of one q-tile (128 rows of head bh) over key tiles [kb, ke).
-// On return acc_o holds this lane's unnormalised O^T (query qrow), m_run the
-// running max (log2 units, scaled) and l_run this lane's half of the row sum.
+// Q operand (B of S^T) of this lane: query qrow of the q-tile, channel
+// d = dk*16 + hf*8 + e; rows past s_q load as zeros.
 template <int D, class P>
-__device__ __forceinline__ void run_qtile(const P &p, char *smem, const Lane<D> &ln, int b, int h, int qt,
-                                          int kb, int ke, f32x16 *acc_o, float &m_run, float &l_run) {
-  using G = Geo<D>;
-  constexpr int DK = D / 16, DB = D / 32;
+__device__ __forceinline__ void load_q(const P &p, const Lane<D> &ln, int b, int h, int qt, bf16x8 *qop) {
+  constexpr int DK = D / 16;
   const bf16_t *qbase = p.q + b * p.qs_b + h * p.qs_h;
+  const int qrow = qt * BM + ln.wave * 32 + ln.l32;
+  u32x4 raw[DK];
+  const bool in_q = qrow < p.s_q;
+  const bf16_t *qr = qbase + (int64_t)(in_q ? qrow : 0) * p.qs_s;
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) raw[dk] = in_q ? ldg16(qr + dk * 16 + ln.hf * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) qop[dk] = __builtin_bit_cast(bf16x8, raw[dk]);
+}
+
+// Attention of one q-tile (BM rows of head (b, h)) over the key tiles
+// [kb, ke), whose rows at or past kv_end are pads (they are fetched as zeros
+// and masked). FIRST: the first key range of the q-tile: Q is loaded into
+// qop (while the first K/V tiles are in flight) and the running state starts
+// from this range; otherwise qop is already loaded and the range continues
+// the running state (a raised maximum rescales O and l). On return acc_o
+// holds this lane's unnormalised O^T (query qrow), m_run the running max
+// (log2 units, scaled) and l_run this lane's half of the row sum.
+template <int D, bool FIRST, class P>
+__device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &ln, int b, int h, int qt, int kb,
+                                         int ke, int kv_end, bf16x8 *qop, f32x16 *acc_o, float &m_run,
+                                         float &l_run) {
+  using G = Geo<D>;
+  constexpr int DB = D / 32;
   const bf16_t *kbase = p.k + b * p.ks_b + h * p.ks_h;
   const bf16_t *vbase = p.v + b * p.vs_b + h * p.vs_h;
-  const int kv_valid = p.kv_valid;
 
   const uint32_t wbase = (uint32_t)(uintptr_t)(lds_void_t *)smem + ln.wave * G::LOADS_PER_WAVE * 1024;
-  issue_rows<D, G::K0>(wbase, kbase, ln.ks_bytes, kb, kv_valid, ln.koff);
-  issue_rows<D, G::V0>(wbase, vbase, ln.vs_bytes, kb, kv_valid, ln.voff);
-  if (kb + 1 < ke) issue_rows<D, G::K0 + G::TILE_BYTES>(wbase, kbase, ln.ks_bytes, kb + 1, kv_valid, ln.koff);
+  issue_rows<D, G::K0>(wbase, kbase, ln.ks_bytes, kb, kv_end, ln.koff);
+  issue_rows<D, G::V0>(wbase, vbase, ln.vs_bytes, kb, kv_end, ln.voff);
+  if (kb + 1 < ke) issue_rows<D, G::K0 + G::TILE_BYTES>(wbase, kbase, ln.ks_bytes, kb + 1, kv_end, ln.koff);
 
-  // ---- Q operand (B of S^T): lane holds query qrow, d = dk*16 + hf*8 + e.
-  const int qrow = qt * BM + ln.wave * 32 + ln.l32;
-  bf16x8 qop[DK];
-  {
-    u32x4 raw[DK];
-    const bool in_q = qrow < p.s_q;
-    const bf16_t *qr = qbase + (int64_t)(in_q ? qrow : 0) * p.qs_s;
+  if (FIRST) {
+    load_q<D>(p, ln, b, h, qt, qop);
+    l_run = 0.f;
 #pragma unroll
-    for (int dk = 0; dk < DK; ++dk) raw[dk] = in_q ? ldg16(qr + dk * 16 + ln.hf * 8) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) qop[dk] = __builtin_bit_cast(bf16x8, raw[dk]);
+    for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
   }
-
-  l_run = 0.f;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
   const float c2 = p.scale_log2;
   f32x16 sa[2], sb[2];
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K(kb), V(kb), K(kb+1) landed
   __syncthreads();
   qk_tile<D>(smem + G::K0, ln.kx, qop, sa);
   __syncthreads();                      // K(kb)'s buffer is refilled by the first step
-  if ((kb + 1) * BN > kv_valid) mask_tail(sa, kb * BN, kv_valid, ln.hf);
-  m_run = pair_max(sa) * c2;            // first tile: nothing accumulated yet
+  if ((kb + 1) * BN > kv_end) mask_tail(sa, kb * BN, kv_end, ln.hf);
+  if (FIRST) {
+    m_run = pair_max(sa) * c2;          // first tile: nothing accumulated yet
+  } else {
+    const float mt = pair_max(sa) * c2;
+    const bool upd = mt > m_run + kLazyRescale;
+    if (__any(upd)) {
+      const float m_new = upd ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+      m_run = m_new;
+    }
+  }
 
   StepCtx<D> cx{smem, wbase, kbase, vbase, ln.koff, ln.voff, ln.kx, ln.vx, qop,
-                ln.ks_bytes, ln.vs_bytes, kv_valid, ke, ln.wave, ln.hf, c2};
+                ln.ks_bytes, ln.vs_bytes, kv_end, ke, ln.wave, ln.hf, c2};
   // steady state: tiles t, t+1, t+2 all full; two tiles per iteration so the
   // score registers alternate roles and the LDS buffer parity is static
   int t = kb;
@@ -364,8 +387,24 @@ __device__ __forceinline__ void run_qtile(const P &p, char *smem, const Lane<D> 
   // masked tail
   for (; t < ke; ++t) {
     const bool has_next = t + 1 < ke;
-    step<D, false>(cx, t, (t - kb) & 1, sa, sb, acc_o, m_run, l_run, has_next, has_next && (t + 2) * BN > kv_valid);
+    step<D, false>(cx, t, (t - kb) & 1, sa, sb, acc_o, m_run, l_run, has_next, has_next && (t + 2) * BN > kv_end);
   }
+}
+
+// One q-tile over the key tiles [kb, ke) of a key range whose real rows end
+// at kv_valid.
+template <int D, class P>
+__device__ __forceinline__ void run_qtile(const P &p, char *smem, const Lane<D> &ln, int b, int h, int qt,
+                                          int kb, int ke, f32x16 *acc_o, float &m_run, float &l_run) {
+  bf16x8 qop[D / 16];
+  run_keys<D, true>(p, smem, ln, b, h, qt, kb, ke, p.kv_valid, qop, acc_o, m_run, l_run);
+}
+
+// Whether query row qrow is a real token: q_valid counts the real rows of
+// the whole sequence, or of each q_seg_len-row segment when q_seg_len > 0.
+template <class P>
+__device__ __forceinline__ bool query_is_real(const P &p, int qrow) {
+  return p.q_seg_len > 0 ? (qrow < p.s_q && qrow % p.q_seg_len < p.q_valid) : qrow < p.q_valid;
 }
 
 __device__ __forceinline__ float pair_sum(float x) {
@@ -546,7 +585,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
       for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
     }
     const float l_tot = pair_sum(l_run);
-    const bool row_ok = (qrow < p.q_valid) && (nk > 0);
+    const bool row_ok = query_is_real(p, qrow) && (nk > 0);
     store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
     return;
   }
@@ -567,7 +606,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   run_qtile<D>(p, smem, ln, b, h, qt, kb, ke, acc_o, m_run, l_run);
   const float l_tot = pair_sum(l_run);
   const float lse2 = m_run + __log2f(l_tot);
-  const bool row_ok = qrow < p.q_valid;
+  const bool row_ok = query_is_real(p, qrow);
   // partial: O / l (fp32, in this lane's accumulator layout) and log2 LSE,
   // written agent-coherent; the arrival counter is bumped once every
   // thread's stores completed.
@@ -594,6 +633,47 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   }
   __syncthreads();
   if (last_flag) merge_pieces<D>(p, ln, T, s, b, h, qrow, row_ok, acc_o, lse2);
+}
+
+// Keys in n_kv_seg segments of kv_seg_len rows (a multiple of the key tile),
+// each holding kv_valid real rows followed by its own tail pad (the ring
+// layout of maxdiffusion PR #491, each ring segment padded at its own tail):
+// one workgroup per q-tile runs the key tiles of every segment's real rows in
+// turn, continuing one online softmax, so the result is the softmax over the
+// union of the real keys.
+template <int D>
+__global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_seg_kernel(AttnParams p) {
+  using G = Geo<D>;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * G::TILE_BYTES];
+
+  Lane<D> ln;
+  make_lane<D>(p, threadIdx.x, ln);
+  const int tps = (p.kv_valid + BN - 1) / BN;   // key tiles with real rows, per segment
+  const int seg_tiles = p.kv_seg_len / BN;
+  f32x16 acc_o[DB];
+  float m_run = -INFINITY, l_run = 0.f;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = logical % p.n_qtiles;
+  const int bh = logical / p.n_qtiles;
+  const int h = bh % p.H, b = bh / p.H;
+  const int qrow = qt * BM + ln.wave * 32 + ln.l32;
+  if (tps > 0) {
+    bf16x8 qop[D / 16];
+    run_keys<D, true>(p, smem, ln, b, h, qt, 0, tps, p.kv_valid, qop, acc_o, m_run, l_run);
+    for (int sg = 1; sg < p.n_kv_seg; ++sg) {
+      __syncthreads();   // every wave is done with the previous range's LDS tiles
+      const int kb = sg * seg_tiles;
+      run_keys<D, false>(p, smem, ln, b, h, qt, kb, kb + tps, sg * p.kv_seg_len + p.kv_valid, qop, acc_o, m_run,
+                         l_run);
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
+  }
+  const float l_tot = pair_sum(l_run);
+  const bool row_ok = query_is_real(p, qrow) && (tps > 0);
+  store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
 }
 
 // Pre-pass of Q and K (blockIdx.y picks the tensor): optional per-head RMS
@@ -690,6 +770,13 @@ hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t stream) {
 }
 
 hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream) {
+  if (p.kv_seg_len > 0) {
+    const int64_t nb = (int64_t)p.n_qtiles * p.H * p.B;
+    if (nb <= 0) return hipSuccess;
+    if (d == 128) hipLaunchKernelGGL(attn_fwd_seg_kernel<128>, dim3((unsigned)nb), dim3(NT), 0, stream, p);
+    else hipLaunchKernelGGL(attn_fwd_seg_kernel<64>, dim3((unsigned)nb), dim3(NT), 0, stream, p);
+    return hipGetLastError();
+  }
   const bool bal = p.sk_splits > 1;
   const int64_t nblocks = (int64_t)p.n_qtiles * p.H * p.B * (bal ? p.sk_splits : 1);
   if (nblocks <= 0) return hipSuccess;

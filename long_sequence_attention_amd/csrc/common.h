@@ -44,6 +44,9 @@ struct AttnParams {
   int64_t vs_b, vs_h, vs_s;
   int64_t os_b, os_h, os_s;
   int32_t B, H, s_q, s_kv, q_valid, kv_valid;
+  // segments padded at their own tails (0 = one segment): q_valid / kv_valid
+  // then count the real rows of each segment
+  int32_t q_seg_len, kv_seg_len, n_kv_seg;
   int32_t o_f32;
   int32_t n_qtiles;
   float scale_log2;  // sm_scale * log2(e)

@@ -76,6 +76,13 @@ def _desc(**kw):
     (dict(q_norm_w=0x20000000, norm_eps=-1.0), -1, b"norm_eps"),
     (dict(k_norm_w=0x20000000, norm_eps=float("inf")), -1, b"norm_eps"),
     (dict(k_norm_w=0x20000004, norm_eps=1e-6), -2, b"16-byte aligned"),
+    (dict(kv_seg_len=100), -1, b"multiple of kv_seg_len"),
+    (dict(q_seg_len=96), -1, b"multiple of q_seg_len"),
+    (dict(kv_seg_len=128, kv_valid=129), -1, b"kv_valid"),
+    (dict(q_seg_len=128, q_valid=200), -1, b"q_valid"),
+    (dict(kv_seg_len=32, kv_valid=32), -2, b"key tile"),
+    (dict(kv_seg_len=128, kv_valid=100, schedule=2), -2, b"balanced"),
+    (dict(kv_seg_len=-1), -1, b"segment lengths"),
 ])
 def test_attn_fwd_rejects_bad_arguments_before_any_hip_call(L, kw, code, msg):
     d = _desc(**kw)

@@ -165,6 +165,113 @@ def test_fused_qk_rmsnorm_rope(ops, case):
     assert_pad_rows(og, lg, valid, "fused norm")
 
 
+def _segmented_inputs(w, n_seg, seg_len, seed):
+    """The workload's real tokens cut into n_seg equal runs, each padded at its
+    own tail to seg_len rows with garbage: the ring layout. Returns Q, K, V
+    bits [B, H, n_seg*seg_len, d], the positions (pads at 0) and the count of
+    real rows per segment."""
+    q, k, v = W.make_qkv(w)
+    per = w.s_valid // n_seg
+    assert per * n_seg == w.s_valid and per <= seg_len
+    pos = W.positions(w)
+    r = np.random.default_rng(seed)
+    outs = []
+    for x in (q, k, v):
+        y = W.finite_garbage_bits(r, (w.B, w.H, n_seg * seg_len, w.d))
+        for i in range(n_seg):
+            y[:, :, i * seg_len:i * seg_len + per] = x[:, :, i * per:(i + 1) * per]
+        outs.append(y)
+    ps = np.zeros((n_seg * seg_len, pos.shape[1]), np.int32)
+    for i in range(n_seg):
+        ps[i * seg_len:i * seg_len + per] = pos[i * per:(i + 1) * per]
+    return outs[0], outs[1], outs[2], ps, per
+
+
+def test_segmented_ring_layout_wan480(ops):
+    """Wan 480p tokens as two ring segments of 2340 real rows each padded to
+    2368 (maxdiffusion PR #491: each ring segment padded at its own tail),
+    queries and keys alike, RoPE on both: one call gives the softmax over
+    every real key, graded at the bar; pad rows 0 / -inf; NaN / Inf refills
+    of every pad row change no bit; and it matches the merge of the two
+    per-segment calls."""
+    import torch
+    w = W.WORKLOADS["wan480"]
+    say("segmented wan480: 2 x (2340 real -> 2368)")
+    q, k, v, pos, per = _segmented_inputs(w, 2, 2368, 52)
+    S = q.shape[2]
+    tabs = ops.rope_split_tables(torch.from_numpy(pos).to(dev()), w.axes, w.d, w.theta)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    o, l = ops.attn_fwd(qd, kd, vd, q_valid=per, kv_valid=per, q_seg_len=2368, kv_seg_len=2368,
+                        rope_q=tabs, rope_k=tabs)
+    torch.cuda.synchronize()
+    c_, s_ = oracle.rope_tables(pos, w.axes, w.theta)
+    qf = oracle.rope_split_halves(oracle.bf16_to_f64(q), c_, s_)
+    kf = oracle.rope_split_halves(oracle.bf16_to_f64(k), c_, s_)
+    O_ref, L_ref = oracle.attention_segmented(qf, kf, oracle.bf16_to_f64(v), 2368, per, 2368, per)
+    valid = np.zeros(S, bool)
+    valid[oracle.segment_valid_rows(S, 2368, per)] = True
+    og, lg = to_np_f64(o), to_np_f64(l)
+    compare(og, lg, O_ref, L_ref, valid, "segmented wan480")
+    assert_pad_rows(og, lg, valid, "segmented wan480")
+    # pads refilled with NaN / Inf: identical bits
+    for fill in (0x7FC0, 0xFF80):
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        for x in (q2, k2, v2):
+            x[:, :, ~valid] = fill
+        o2, l2 = ops.attn_fwd(to_dev_bf16(q2), to_dev_bf16(k2), to_dev_bf16(v2), q_valid=per, kv_valid=per,
+                              q_seg_len=2368, kv_seg_len=2368, rope_q=tabs, rope_k=tabs)
+        torch.cuda.synchronize()
+        assert np.array_equal(raw_bits(o2)[:, :, valid], raw_bits(o)[:, :, valid])
+        assert np.array_equal(raw_bits(l2)[:, :, valid], raw_bits(l)[:, :, valid])
+        assert_pad_rows(to_np_f64(o2), to_np_f64(l2), valid, "segmented refill")
+    # the merge of the two per-segment calls (fp32 partials) agrees to rounding
+    po, pl = [], []
+    for i in range(2):
+        sl = slice(i * 2368, (i + 1) * 2368)
+        tk = (tabs[0][sl].contiguous(), tabs[1][sl].contiguous())
+        oi, li = ops.attn_fwd(qd, kd[:, :, sl], vd[:, :, sl], q_valid=per, kv_valid=per, q_seg_len=2368,
+                              rope_q=tabs, rope_k=tk, out_dtype=torch.float32)
+        po.append(oi)
+        pl.append(li)
+    om, lm = ops.lse_merge(po, pl)
+    torch.cuda.synchronize()
+    dO = np.abs(to_np_f64(om) - og)[:, :, valid].max()
+    dL = np.abs(to_np_f64(lm) - lg)[:, :, valid].max()
+    print(f"[segmented vs merge] O {dO:.2e} LSE {dL:.2e}", flush=True)
+    assert dO < 1e-2 and dL < 1e-4
+
+
+@pytest.mark.parametrize("case", [
+    dict(n_seg=3, seg_len=128, per=128, d=128),   # real rows fill the segment: no masked tile
+    dict(n_seg=4, seg_len=192, per=1, d=128),     # one real key per segment
+    dict(n_seg=2, seg_len=320, per=257, d=64),    # d = 64, masked tail tile in each segment
+])
+def test_segmented_edge_cases(ops, case):
+    import torch
+    say(f"segmented edge {case}")
+    n, L, per, d = case["n_seg"], case["seg_len"], case["per"], case["d"]
+    r = np.random.default_rng(53)
+    S = n * L
+    q = W.bf16_bits(r.standard_normal((1, 2, S, d)).astype(np.float32))
+    k = W.bf16_bits(r.standard_normal((1, 2, S, d)).astype(np.float32))
+    v = W.bf16_bits(r.standard_normal((1, 2, S, d)).astype(np.float32))
+    valid = np.zeros(S, bool)
+    valid[oracle.segment_valid_rows(S, L, per)] = True
+    for x in (k, v):
+        x[:, :, ~valid] = W.finite_garbage_bits(r, x[:, :, ~valid].shape)
+    o, l = ops.attn_fwd(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), q_valid=per, kv_valid=per,
+                        q_seg_len=L, kv_seg_len=L)
+    torch.cuda.synchronize()
+    qf, kf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(k)
+    O_ref, L_ref = oracle.attention_segmented(qf, kf, oracle.bf16_to_f64(v), L, per, L, per)
+    bound = lse_rounding_bound(qf[:, :, valid], kf[:, :, valid], int(valid.sum()), 1.0 / math.sqrt(d))
+    lse_tol = np.full(L_ref.shape, 5e-3)
+    lse_tol[:, :, valid] = bound
+    og, lg = to_np_f64(o), to_np_f64(l)
+    compare(og, lg, O_ref, L_ref, valid, f"segmented edge {case}", lse_tol=lse_tol)
+    assert_pad_rows(og, lg, valid, "segmented edge")
+
+
 def test_short_kv_cross_attention(ops):
     """Video queries over 512 text keys (no RoPE): the short-KV regime of the
     Wan cross-attention (maxdiffusion PR #491, fused short-KV cross-attention
