@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--hbm-passes", action="store_true",
+                    help="time the HBM-bound passes (pad, unpad, LSE merge, tables) on Wan 720p-sized buffers")
     return ap.parse_args()
 
 
@@ -148,6 +150,41 @@ def pmc_target(args):
         ops.pad_tokens(src.view(1, rows, 4096), rows, out=dst.view(1, rows, 4096))
     torch.cuda.synchronize()
     print("pmc target done", flush=True)
+
+
+def hbm_passes(args):
+    """The HBM-bound passes on Wan 720p-sized buffers (larger than the 256 MB
+    MALL, so the figures are HBM rates): pad and unpad of one token-major
+    tensor [1, S, 10, 128] bf16, the 4-part fp32 -> bf16 LSE merge, and the
+    RoPE tables. Prints one JSON line of average µs and GB/s per pass (HIP
+    events over 20 back-to-back calls after 5 warm-up calls); run under
+    rocprofv3 --kernel-trace for the per-kernel durations."""
+    import torch
+    import workloads as W
+    import long_sequence_attention_amd as ops
+    ops.library_path()
+    w = W.WORKLOADS["wan720"]
+    dev = torch.device("cuda:0")
+    Sv, Sp, H, d = w.s_valid, w.s_pad, w.H, w.d
+    x = torch.randn((1, Sv, H, d), device=dev).to(torch.bfloat16)
+    xp = torch.empty((1, Sp, H, d), dtype=torch.bfloat16, device=dev)
+    xu = torch.empty_like(x)
+    parts_o = [torch.randn((1, H, Sp, d), device=dev) for _ in range(4)]
+    parts_l = [torch.randn((1, H, Sp), device=dev) for _ in range(4)]
+    om = torch.empty((1, H, Sp, d), dtype=torch.bfloat16, device=dev)
+    lm = torch.empty((1, H, Sp), dtype=torch.float32, device=dev)
+    pos = torch.from_numpy(W.positions(w)).to(dev)
+    row = H * d * 2
+    res = {}
+    for name, fn, nbytes in (
+            ("pad_tokens", lambda: ops.pad_tokens(x, Sp, out=xp), (Sv + Sp) * row),
+            ("unpad_tokens", lambda: ops.unpad_tokens(xp, Sv, out=xu), 2 * Sv * row),
+            ("lse_merge_4xf32_to_bf16", lambda: ops.lse_merge(parts_o, parts_l, q_valid=Sv, out=om, lse_out=lm),
+             4 * H * Sp * (d * 4 + 4) + H * Sp * (d * 2 + 4)),
+            ("rope_split_tables", lambda: ops.rope_split_tables(pos, w.axes, d, w.theta), Sp * d // 2 * 8)):
+        us = time_us(torch, fn, 20, warm=5)
+        res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / us / 1e3}
+    print(json.dumps({"hbm_passes_wan720": res}), flush=True)
 
 
 def traffic_summary(args):
@@ -283,6 +320,9 @@ def main():
         return
     if args.pmc_target:
         pmc_target(args)
+        return
+    if args.hbm_passes:
+        hbm_passes(args)
         return
     import ctypes
     import numpy as np

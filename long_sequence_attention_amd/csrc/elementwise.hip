@@ -32,10 +32,12 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(TableParams p) {
 // Tail pad / unpad of one batch (blockIdx.y): rows 0..n_copy-1 of both
 // sides are one contiguous run, so out[i] = in[i] for i < n_copy granules
 // and out[i] = 0 up to n_total. V is the copy granule (16, 4 or 1 bytes),
-// chosen from the row size and alignment. Each thread keeps UNROLL granules
-// in flight, a grid stride apart, so consecutive lanes stay on consecutive
-// addresses.
-template <typename V, int UNROLL>
+// chosen from the row size and alignment. UNROLL granules per thread are in
+// flight, a grid stride apart, so consecutive lanes stay on consecutive
+// addresses. STREAM: the source is read with non-temporal loads (it is dead
+// after the copy; the result is stored normally, so the next kernel can
+// still find it in the caches).
+template <typename V, int UNROLL, bool STREAM>
 __global__ __launch_bounds__(256) void row_copy_kernel(const V *__restrict__ in, V *__restrict__ out,
                                                       int64_t in_batch, int64_t out_batch, int64_t n_copy,
                                                       int64_t n_total) {
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void row_copy_kernel(const V *__restrict__ in,
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t i = i0 + u * stride;
-      v[u] = (i < n_copy) ? src[i] : V{};
+      v[u] = (i < n_copy) ? (STREAM ? __builtin_nontemporal_load(src + i) : src[i]) : V{};
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
@@ -57,42 +59,54 @@ __global__ __launch_bounds__(256) void row_copy_kernel(const V *__restrict__ in,
   }
 }
 
-// 32 lanes per (b, h, i) row; each lane owns d/32 consecutive channels.
 template <int PER>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   if (row >= p.rows) return;
   const int sub = threadIdx.x & 31;
   const int i = (int)(row % p.S);
+  const int64_t off = row * p.d + sub * PER;
+  // every part's LSE and O chunk is requested before any arithmetic, so a
+  // thread keeps n_parts loads in flight (the partials are read once:
+  // non-temporal loads)
   float L[kMaxMergeParts];
-  float M = -INFINITY;
-  for (int k = 0; k < p.n_parts; ++k) {
-    L[k] = p.lse_parts[k][row];
-    M = fmaxf(M, L[k]);
+  float val[kMaxMergeParts][PER];
+#pragma unroll
+  for (int k = 0; k < kMaxMergeParts; ++k) {
+    if (k < p.n_parts) {
+      L[k] = p.lse_parts[k][row];
+      if (p.part_f32) {
+        const float *src = reinterpret_cast<const float *>(p.o_parts[k]) + off;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) val[k][e] = __builtin_nontemporal_load(src + e);
+      } else {
+        const bf16_t *src = reinterpret_cast<const bf16_t *>(p.o_parts[k]) + off;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) val[k][e] = __uint_as_float((uint32_t)__builtin_nontemporal_load(src + e) << 16);
+      }
+    }
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxMergeParts; ++k)
+    if (k < p.n_parts) M = fmaxf(M, L[k]);
   const bool empty = (M == -INFINITY) || (i >= p.q_valid);
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (!empty) {
-    for (int k = 0; k < p.n_parts; ++k) {
-      const float w = expf(L[k] - M);
-      wsum += w;
-      const int64_t off = row * p.d + sub * PER;
-      if (p.part_f32) {
-        const float *src = reinterpret_cast<const float *>(p.o_parts[k]) + off;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, src[e], acc[e]);
-      } else {
-        const bf16_t *src = reinterpret_cast<const bf16_t *>(p.o_parts[k]) + off;
+    for (int k = 0; k < kMaxMergeParts; ++k) {
+      if (k < p.n_parts) {
+        const float w = expf(L[k] - M);
+        wsum += w;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, __uint_as_float((uint32_t)src[e] << 16), acc[e]);
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, val[k][e], acc[e]);
       }
     }
   }
   const float inv = empty ? 0.f : 1.0f / wsum;
-  const int64_t off = row * p.d + sub * PER;
   if (p.out_f32) {
     float *dst = reinterpret_cast<float *>(p.o_out) + off;
 #pragma unroll
@@ -123,24 +137,39 @@ hipError_t launch_rope_tables(const TableParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Copies that fit the 256 MB MALL (the Wan 480p / FLUX token tensors) run
+// four granules per thread on at most 4096 blocks; larger ones stream one
+// granule per thread on up to 32768 blocks with non-temporal source loads
+// (measured on MI355X: 6.8 TB/s against 4.8 TB/s for the small-copy form
+// on a 387 MB pad, while the small-copy form makes the Wan 480p step, with
+// its three pads and one unpad of 24 MB each, about 1 us faster).
 template <typename V>
 static void launch_copy_v(const void *in, void *out, int B, int s_in, int s_out, int n_copy, int64_t row_bytes,
                           hipStream_t stream) {
-  constexpr int UNROLL = 4;
   const int64_t rv = row_bytes / (int64_t)sizeof(V);
   const int64_t n_total = (int64_t)s_out * rv;
-  int64_t blocks = (n_total + 256 * UNROLL - 1) / (256 * UNROLL);
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL((row_copy_kernel<V, UNROLL>), dim3((unsigned)blocks, (unsigned)B), dim3(256), 0, stream,
-                     static_cast<const V *>(in), static_cast<V *>(out), (int64_t)s_in * rv, n_total,
-                     (int64_t)n_copy * rv, n_total);
+  const bool large = (int64_t)B * n_total * (int64_t)sizeof(V) * 2 > (128LL << 20);
+  const dim3 blk(256);
+  const V *src = static_cast<const V *>(in);
+  V *dst = static_cast<V *>(out);
+  if (large) {
+    int64_t blocks = (n_total + 255) / 256;
+    if (blocks > 32768) blocks = 32768;
+    hipLaunchKernelGGL((row_copy_kernel<V, 1, true>), dim3((unsigned)blocks, (unsigned)B), blk, 0, stream, src, dst,
+                       (int64_t)s_in * rv, n_total, (int64_t)n_copy * rv, n_total);
+  } else {
+    int64_t blocks = (n_total + 1023) / 1024;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL((row_copy_kernel<V, 4, false>), dim3((unsigned)blocks, (unsigned)B), blk, 0, stream, src,
+                       dst, (int64_t)s_in * rv, n_total, (int64_t)n_copy * rv, n_total);
+  }
 }
 
 hipError_t launch_row_copy(const void *in, void *out, int B, int s_in, int s_out, int n_copy,
                            int64_t row_bytes, hipStream_t stream) {
   if ((int64_t)B * s_out * row_bytes == 0) return hipSuccess;
   const uintptr_t a = reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out);
-  if (row_bytes % 16 == 0 && a % 16 == 0) launch_copy_v<uint4>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
+  if (row_bytes % 16 == 0 && a % 16 == 0) launch_copy_v<u32x4>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
   else if (row_bytes % 4 == 0 && a % 4 == 0) launch_copy_v<uint32_t>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
   else launch_copy_v<uint8_t>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
   return hipGetLastError();
