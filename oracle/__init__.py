@@ -29,6 +29,11 @@ What each function follows (pages are cited by title and section):
     padding per ring segment on the Ulysses-ring path; the padding
     descriptor carries the real length and the segment count), attended as
     one softmax over every real key.
+  * fixed_m_bound -- the a-priori row-max bound of the fixed-m softmax
+    (maxdiffusion PR #491: fixed-m metadata from norm reductions and the key
+    mean over the real rows, with an online-softmax fallback). The formula
+    is not printed on the pages; the plain Cauchy-Schwarz reading
+    scale * (q.kbar + |q| max_j |k_j - kbar|) is used.
   * lse_merge -- combining per-key-shard (O, LSE) pairs into the single-pass
     result (mstar PR #376, attention_over_sharded_keys).
   * pad_tokens / unpad_tokens / plan_padding -- tail padding of token rows to
@@ -52,6 +57,7 @@ from .reference import (  # noqa: F401
     attention_bruteforce,
     segment_valid_rows,
     attention_segmented,
+    fixed_m_bound,
     lse_merge,
     dit_path,
 )

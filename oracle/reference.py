@@ -199,6 +199,31 @@ def attention_segmented(q, k, v, q_seg_len: int, q_valid: int, kv_seg_len: int, 
     return O, L
 
 
+def fixed_m_bound(q, k, key_rows, scale: float | None = None) -> np.ndarray:
+    """A-priori upper bound of each query row's largest score, float64:
+
+        m_i = scale * (q_i . kbar + |q_i| * max_j |k_j - kbar|),
+        kbar = mean of the real keys k_j (j in key_rows)
+
+    since q_i . k_j = q_i . kbar + q_i . (k_j - kbar) <= q_i . kbar +
+    |q_i| |k_j - kbar| (Cauchy-Schwarz). The fixed-m softmax uses it in place
+    of the running maximum (maxdiffusion PR #491 builds it from norm
+    reductions and the key mean over the real rows only, and sends a block
+    whose bound is too loose to the online-softmax path). The pages do not
+    print the formula; this is the plain reading. q: [B, H, S_q, d];
+    k: [B, H, S_kv, d]; returns [B, H, S_q].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)[:, :, np.asarray(key_rows)]
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kbar = k.mean(axis=2, keepdims=True)                           # [B, H, 1, d]
+    R = np.sqrt(((k - kbar) ** 2).sum(axis=-1)).max(axis=2)         # [B, H]
+    qn = np.sqrt((q * q).sum(axis=-1))                              # [B, H, S_q]
+    return scale * ((q @ np.swapaxes(kbar, -1, -2))[..., 0] + qn * R[..., None])
+
+
 def attention_bruteforce(q, k, v, q_valid: int, kv_valid: int, scale: float | None = None):
     """The same definition as `attention`, in pure-Python loops (tiny sizes)."""
     q = np.asarray(q, dtype=np.float64)

@@ -366,6 +366,42 @@ def test_segmented_pads_and_segment_order_do_not_matter():
     assert (O[:, :, qpad] == 0).all() and np.isneginf(L[:, :, qpad]).all()
 
 
+# ------------------------------------------------------------------ fixed-m bound
+def test_fixed_m_bound_bounds_every_score():
+    r = rng(40)
+    q = r.standard_normal((1, 3, 50, 32)) * 2.0
+    k = r.standard_normal((1, 3, 70, 32)) + 1.5   # keys with a common mean
+    rows = np.arange(61)
+    m = oracle.fixed_m_bound(q, k, rows)
+    s = np.einsum("bhqd,bhkd->bhqk", q, k[:, :, rows]) / math.sqrt(32)
+    assert (m >= s.max(axis=-1) - 1e-12).all()
+
+
+def test_fixed_m_bound_is_tight_for_identical_keys_and_shifts_with_the_mean():
+    r = rng(41)
+    q = r.standard_normal((1, 1, 8, 16))
+    c = r.standard_normal(16)
+    k = np.broadcast_to(c, (1, 1, 10, 16)).copy()
+    m = oracle.fixed_m_bound(q, k, np.arange(10), scale=1.0)
+    assert np.allclose(m, (q @ c)[..., :], rtol=0, atol=1e-12)     # R = 0: the bound is the score
+    k2 = r.standard_normal((1, 1, 10, 16))
+    mu = 3.0 * r.standard_normal(16)
+    m1 = oracle.fixed_m_bound(q, k2, np.arange(10), scale=1.0)
+    m2 = oracle.fixed_m_bound(q, k2 + mu, np.arange(10), scale=1.0)
+    assert np.allclose(m2 - m1, q @ mu, rtol=0, atol=1e-12)          # a common key shift moves it by q.mu
+
+
+def test_fixed_m_bound_ignores_pad_rows():
+    r = rng(42)
+    q = r.standard_normal((1, 2, 5, 8))
+    k = r.standard_normal((1, 2, 20, 8))
+    rows = oracle.segment_valid_rows(20, 10, 7)
+    m = oracle.fixed_m_bound(q, k, rows)
+    k2 = k.copy()
+    k2[:, :, [7, 8, 9, 17, 18, 19]] = 1e6
+    assert np.array_equal(oracle.fixed_m_bound(q, k2, rows), m)
+
+
 # ------------------------------------------------------------------ merge
 def _shards(q, k, v, cuts, q_valid, total_valid):
     parts = []
