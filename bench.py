@@ -251,6 +251,14 @@ def config_table(np, torch, ops, W, dev, n_iter):
                                                  rope_q=tabs, rope_k=tabs, out=o, lse=lse,
                                                  workspace=ws), n)
         ent = {"us": us, "tflops": w.valid_flop / us / 1e6, "pct_peak": w.valid_flop / us / 1e6 / PEAK_BF16_TFLOPS * 100}
+        if name in ("wan480", "hunyuan", "wan720"):   # the fixed-m softmax (key / query statistics passes)
+            wsf = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
+                                                          rope_q=tabs, rope_k=tabs, fixed_m=True), 256),
+                              dtype=torch.uint8, device=dev)
+            ent["fixed_m_us"] = time_us(torch, lambda: ops.attn_fwd(
+                qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=tabs, rope_k=tabs, out=o, lse=lse,
+                workspace=wsf, fixed_m=True), n)
+            del wsf
         if name == "wan480":   # the same call with the per-head q/k RMSNorm fused into the pre-pass
             wn = torch.ones(w.d, dtype=torch.float32, device=dev)
             wsn = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,

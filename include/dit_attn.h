@@ -128,6 +128,18 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * and LSE = -inf. s must be a multiple of its segment length and valid <=
  * segment length (else DIT_ERR_INVALID); kv_seg_len must be a multiple of 64
  * and the schedule not BALANCED (else DIT_ERR_UNSUPPORTED).
+ *
+ * fixed_m = 1 (the fixed-m softmax of maxdiffusion PR #491; the bound is not
+ * printed there, the plain reading is used): before the attention kernel,
+ * passes over K (and Q) compute, over the real keys of each head, the key
+ * mean kbar and R = max_j |k_j - kbar|, and for every query row the bound
+ *   m_i = sm_scale * (q_i . kbar + |q_i| R) >= every score of row i
+ * (from the rotated / normalised bf16 Q and K). A q-tile whose real rows all
+ * have 2 sm_scale |q_i| R <= 96 ln 2 uses m_i as its fixed softmax maximum
+ * (no running max, no rescale); any other q-tile keeps the online softmax.
+ * Results agree with the online softmax to rounding and are reproducible
+ * run to run. Needs workspace; not with the BALANCED schedule
+ * (DIT_ERR_UNSUPPORTED). It pays for itself only on long key ranges.
  */
 typedef struct dit_attn_desc {
   int32_t B, H, d;               /* d in {64, 128}, else DIT_ERR_UNSUPPORTED */
@@ -147,6 +159,7 @@ typedef struct dit_attn_desc {
   const float *q_norm_w, *k_norm_w;  /* fp32 [d] RMSNorm weights or NULL (no norm) */
   float norm_eps;
   int32_t q_seg_len, kv_seg_len; /* 0, or segment length: see "Segments" above */
+  int32_t fixed_m;               /* 0 = online softmax, 1 = fixed-m: see above */
 } dit_attn_desc;
 
 /* Bytes of workspace dit_attn_fwd needs for `desc` (0 when K is not rotated

@@ -54,7 +54,7 @@ def plan_padding(s_valid: int, multiple: int) -> int:
 
 
 def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule=0,
-               q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0):
+               q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False):
     B, H, s_q, d = q.shape
     desc = N.AttnDesc()
     desc.B, desc.H, desc.d = B, H, d
@@ -77,16 +77,17 @@ def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, sch
         desc.k_norm_w = k_norm.data_ptr()
     desc.norm_eps = float(norm_eps)
     desc.q_seg_len, desc.kv_seg_len = int(q_seg_len), int(kv_seg_len)
+    desc.fixed_m = 1 if fixed_m else 0
     return desc
 
 
 def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, schedule=0,
-                        q_norm=None, k_norm=None, q_seg_len=0, kv_seg_len=0) -> int:
+                        q_norm=None, k_norm=None, q_seg_len=0, kv_seg_len=0, fixed_m=False) -> int:
     """Workspace bytes attn_fwd needs (dit_attn_workspace_size) on q's device."""
     q_valid = (q_seg_len or q.shape[2]) if q_valid is None else int(q_valid)
     kv_valid = (kv_seg_len or k.shape[2]) if kv_valid is None else int(kv_valid)
     desc = _attn_desc(q, k, v, q, None, q_valid, kv_valid, rope_q, rope_k, 0.0, schedule, q_norm, k_norm,
-                      q_seg_len=q_seg_len, kv_seg_len=kv_seg_len)
+                      q_seg_len=q_seg_len, kv_seg_len=kv_seg_len, fixed_m=fixed_m)
     need = ctypes.c_size_t()
     with torch.cuda.device(q.device):
         N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_workspace_size")
@@ -95,7 +96,7 @@ def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, ro
 
 def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
              out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None, schedule=0,
-             q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0):
+             q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False):
     """Attention forward (dit_attn_fwd).
 
     q: [B, H, s_q, d], k/v: [B, H, s_kv, d] bf16 device tensors, any strides
@@ -105,7 +106,8 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
     q_norm / k_norm: fp32 [d] RMSNorm weights (per-head q/k RMS normalisation
     before RoPE, epsilon norm_eps) or None. q_seg_len / kv_seg_len > 0: the
     rows form segments of that length, each padded at its own tail, and
-    q_valid / kv_valid count the real rows of each segment.
+    q_valid / kv_valid count the real rows of each segment. fixed_m: use the
+    a-priori row-max bound where it is tight enough (dit_attn_desc.fixed_m).
     Returns (O, LSE) with O [B, H, s_q, d] in out_dtype (or `out`) and LSE
     fp32 [B, H, s_q] (natural log), or O alone if return_lse=False.
     """
@@ -140,7 +142,7 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
             if wt.shape != (d,) or not wt.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous fp32 [{d}] tensor")
     desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule, q_norm, k_norm,
-                      norm_eps, q_seg_len, kv_seg_len)
+                      norm_eps, q_seg_len, kv_seg_len, fixed_m)
     need = ctypes.c_size_t()
     with torch.cuda.device(q.device):
         N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")

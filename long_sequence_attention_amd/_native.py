@@ -53,6 +53,7 @@ class AttnDesc(ctypes.Structure):
         ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p),
         ("norm_eps", ctypes.c_float),
         ("q_seg_len", ctypes.c_int32), ("kv_seg_len", ctypes.c_int32),
+        ("fixed_m", ctypes.c_int32),
     ]
 
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libditattn.so")
-SOURCES = ["api.hip", "attn_fwd.hip", "elementwise.hip"]
+SOURCES = ["api.hip", "attn_fwd.hip", "elementwise.hip", "fixed_m.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

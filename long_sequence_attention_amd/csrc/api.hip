@@ -79,6 +79,9 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
                 dit::kAttnBlockN);
   if (d->kv_seg_len > 0 && d->schedule == DIT_SCHED_BALANCED)
     return fail(DIT_ERR_UNSUPPORTED, "the balanced schedule does not cover key segments");
+  if (d->fixed_m != 0 && d->fixed_m != 1) return fail(DIT_ERR_INVALID, "fixed_m=%d must be 0 or 1", d->fixed_m);
+  if (d->fixed_m && d->schedule == DIT_SCHED_BALANCED)
+    return fail(DIT_ERR_UNSUPPORTED, "the balanced schedule does not cover the fixed-m softmax");
   if (d->o_dtype != DIT_BF16 && d->o_dtype != DIT_F32) return fail(DIT_ERR_INVALID, "o_dtype=%d is not a dit_dtype", d->o_dtype);
   if (d->s_q > 0 && (d->q == nullptr || d->o == nullptr)) return fail(DIT_ERR_INVALID, "q and o must be non-NULL when s_q > 0");
   if (d->kv_valid > 0 && (d->k == nullptr || d->v == nullptr))
@@ -128,6 +131,10 @@ struct AttnPlan {
   int splits = 1;           // key-split pieces per q-tile (1 = one workgroup per q-tile)
   size_t part_o_off = 0, part_l_off = 0, count_off = 0;
   int64_t n_counts = 0;
+  // fixed-m statistics (fm = false: online softmax)
+  bool fm = false;
+  int n_chunks = 0, n_real = 0;
+  size_t fm_part_off = 0, fm_kbar_off = 0, fm_r2_off = 0, fm_m_off = 0, fm_ok_off = 0;
   size_t total = 0;
 };
 
@@ -186,6 +193,23 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
     p.count_off = off;
     p.n_counts = nq;
     off += round_up((size_t)nq * sizeof(int32_t), 256);
+  }
+  if (d->fixed_m && d->kv_valid > 0 && d->s_q > 0) {
+    const size_t bh = (size_t)d->B * d->H;
+    const int64_t nqt = (d->s_q + kBlockM - 1) / kBlockM;
+    p.fm = true;
+    p.n_chunks = (d->s_kv + dit::kStatRows - 1) / dit::kStatRows;
+    p.n_real = d->kv_seg_len > 0 ? (d->s_kv / d->kv_seg_len) * d->kv_valid : d->kv_valid;
+    p.fm_part_off = off;
+    off += round_up(bh * p.n_chunks * d->d * sizeof(float), 256);
+    p.fm_kbar_off = off;
+    off += round_up(bh * d->d * sizeof(float), 256);
+    p.fm_r2_off = off;
+    off += round_up(bh * p.n_chunks * sizeof(float), 256);
+    p.fm_m_off = off;
+    off += round_up(bh * (size_t)d->s_q * sizeof(float), 256);
+    p.fm_ok_off = off;
+    off += round_up(bh * (size_t)nqt * sizeof(int32_t), 256);
   }
   p.total = off;
   *pl = p;
@@ -285,6 +309,26 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
     }
     rc = hip_status(dit::launch_rope_rotate(r, st), "rotation launch");
     if (rc != DIT_OK) return rc;
+  }
+  if (pl.fm) {
+    char *ws = static_cast<char *>(d.workspace);
+    dit::FixedMParams f{};
+    f.q = p.q; f.k = p.k;
+    f.qs_b = p.qs_b; f.qs_h = p.qs_h; f.qs_s = p.qs_s;
+    f.ks_b = p.ks_b; f.ks_h = p.ks_h; f.ks_s = p.ks_s;
+    f.B = d.B; f.H = d.H; f.d = d.d; f.s_q = d.s_q; f.s_kv = d.s_kv;
+    f.q_valid = d.q_valid; f.kv_valid = d.kv_valid; f.q_seg_len = d.q_seg_len; f.kv_seg_len = d.kv_seg_len;
+    f.n_chunks = pl.n_chunks; f.n_real = pl.n_real; f.n_qtiles = p.n_qtiles;
+    f.c2 = p.scale_log2;
+    f.part = reinterpret_cast<float *>(ws + pl.fm_part_off);
+    f.kbar = reinterpret_cast<float *>(ws + pl.fm_kbar_off);
+    f.r2 = reinterpret_cast<float *>(ws + pl.fm_r2_off);
+    f.m = reinterpret_cast<float *>(ws + pl.fm_m_off);
+    f.ok = reinterpret_cast<int32_t *>(ws + pl.fm_ok_off);
+    rc = hip_status(dit::launch_fixed_m(f, st), "fixed-m statistics launch");
+    if (rc != DIT_OK) return rc;
+    p.fm_m = f.m;
+    p.fm_ok = f.ok;
   }
   p.sk_splits = pl.splits;
   if (pl.splits > 1) {

@@ -209,7 +209,8 @@ struct StepCtx {
 // STEADY: tile t+1 exists and is full, parity static, scheduled with
 // sched_group_barrier. Otherwise has_next / mask_next are run-time flags
 // (the last tiles of a run) and the next scores are copied into scur.
-template <int D, bool STEADY>
+// FIXED: the row maximum is the fixed-m bound (no running max, no rescale).
+template <int D, bool STEADY, bool FIXED>
 __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x16 *scur, f32x16 *snext,
                                      f32x16 *acc_o, float &m_run, float &l_run, bool has_next = true,
                                      bool mask_next = false) {
@@ -261,7 +262,7 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
     }
   }
   float mts = 0.f;
-  if (HAS_NEXT) mts = pair_max(snext) * cx.c2;
+  if (!FIXED && HAS_NEXT) mts = pair_max(snext) * cx.c2;
   if (STEADY) {
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -281,8 +282,8 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
   l_run += ps0 + ps1;
 
   if (HAS_NEXT) {
-    const bool upd = mts > m_run + kLazyRescale;
-    if (__any(upd)) {
+    const bool upd = !FIXED && mts > m_run + kLazyRescale;
+    if (!FIXED && __any(upd)) {
       const float m_new = upd ? mts : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -332,7 +333,9 @@ __device__ __forceinline__ void load_q(const P &p, const Lane<D> &ln, int b, int
 // the running state (a raised maximum rescales O and l). On return acc_o
 // holds this lane's unnormalised O^T (query qrow), m_run the running max
 // (log2 units, scaled) and l_run this lane's half of the row sum.
-template <int D, bool FIRST, class P>
+// FIXED: the running maximum is the q-tile's fixed-m bound, loaded with Q
+// (the range never raises it).
+template <int D, bool FIRST, bool FIXED, class P>
 __device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &ln, int b, int h, int qt, int kb,
                                          int ke, int kv_end, bf16x8 *qop, f32x16 *acc_o, float &m_run,
                                          float &l_run) {
@@ -346,8 +349,13 @@ __device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &
   issue_rows<D, G::V0>(wbase, vbase, ln.vs_bytes, kb, kv_end, ln.voff);
   if (kb + 1 < ke) issue_rows<D, G::K0 + G::TILE_BYTES>(wbase, kbase, ln.ks_bytes, kb + 1, kv_end, ln.koff);
 
+  float m_fix = 0.f;
   if (FIRST) {
     load_q<D>(p, ln, b, h, qt, qop);
+    if (FIXED) {
+      const int qrow = qt * BM + ln.wave * 32 + ln.l32;
+      m_fix = qrow < p.s_q ? p.fm_m[((int64_t)b * p.H + h) * p.s_q + qrow] : 0.f;
+    }
     l_run = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
@@ -359,7 +367,9 @@ __device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &
   qk_tile<D>(smem + G::K0, ln.kx, qop, sa);
   __syncthreads();                      // K(kb)'s buffer is refilled by the first step
   if ((kb + 1) * BN > kv_end) mask_tail(sa, kb * BN, kv_end, ln.hf);
-  if (FIRST) {
+  if (FIXED) {
+    if (FIRST) m_run = m_fix;
+  } else if (FIRST) {
     m_run = pair_max(sa) * c2;          // first tile: nothing accumulated yet
   } else {
     const float mt = pair_max(sa) * c2;
@@ -380,14 +390,15 @@ __device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &
   // score registers alternate roles and the LDS buffer parity is static
   int t = kb;
   for (; t + 3 < ke; t += 2) {
-    step<D, true>(cx, t, 0, sa, sb, acc_o, m_run, l_run);
-    step<D, true>(cx, t + 1, 1, sb, sa, acc_o, m_run, l_run);
+    step<D, true, FIXED>(cx, t, 0, sa, sb, acc_o, m_run, l_run);
+    step<D, true, FIXED>(cx, t + 1, 1, sb, sa, acc_o, m_run, l_run);
   }
   // the last (at most three) tiles: run-time flags; tile t+1 may be the
   // masked tail
   for (; t < ke; ++t) {
     const bool has_next = t + 1 < ke;
-    step<D, false>(cx, t, (t - kb) & 1, sa, sb, acc_o, m_run, l_run, has_next, has_next && (t + 2) * BN > kv_end);
+    step<D, false, FIXED>(cx, t, (t - kb) & 1, sa, sb, acc_o, m_run, l_run, has_next,
+                          has_next && (t + 2) * BN > kv_end);
   }
 }
 
@@ -397,7 +408,14 @@ template <int D, class P>
 __device__ __forceinline__ void run_qtile(const P &p, char *smem, const Lane<D> &ln, int b, int h, int qt,
                                           int kb, int ke, f32x16 *acc_o, float &m_run, float &l_run) {
   bf16x8 qop[D / 16];
-  run_keys<D, true>(p, smem, ln, b, h, qt, kb, ke, p.kv_valid, qop, acc_o, m_run, l_run);
+  run_keys<D, true, false>(p, smem, ln, b, h, qt, kb, ke, p.kv_valid, qop, acc_o, m_run, l_run);
+}
+
+// Whether q-tile qt of head (b, h) runs with the fixed-m bound (set up and
+// found tight enough by launch_fixed_m); uniform over the workgroup.
+template <class P>
+__device__ __forceinline__ bool use_fixed_m(const P &p, int b, int h, int qt) {
+  return p.fm_m != nullptr && p.fm_ok[((int64_t)b * p.H + h) * p.n_qtiles + qt] != 0;
 }
 
 // Whether query row qrow is a real token: q_valid counts the real rows of
@@ -579,7 +597,11 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
     const int h = bh % p.H, b = bh / p.H;
     const int qrow = qt * BM + ln.wave * 32 + ln.l32;
     if (nk > 0) {
-      run_qtile<D>(p, smem, ln, b, h, qt, 0, nk, acc_o, m_run, l_run);
+      bf16x8 qop[D / 16];
+      if (use_fixed_m(p, b, h, qt))
+        run_keys<D, true, true>(p, smem, ln, b, h, qt, 0, nk, p.kv_valid, qop, acc_o, m_run, l_run);
+      else
+        run_keys<D, true, false>(p, smem, ln, b, h, qt, 0, nk, p.kv_valid, qop, acc_o, m_run, l_run);
     } else {
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
@@ -660,12 +682,22 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_seg_kernel(AttnParams p
   const int qrow = qt * BM + ln.wave * 32 + ln.l32;
   if (tps > 0) {
     bf16x8 qop[D / 16];
-    run_keys<D, true>(p, smem, ln, b, h, qt, 0, tps, p.kv_valid, qop, acc_o, m_run, l_run);
-    for (int sg = 1; sg < p.n_kv_seg; ++sg) {
-      __syncthreads();   // every wave is done with the previous range's LDS tiles
-      const int kb = sg * seg_tiles;
-      run_keys<D, false>(p, smem, ln, b, h, qt, kb, kb + tps, sg * p.kv_seg_len + p.kv_valid, qop, acc_o, m_run,
-                         l_run);
+    if (use_fixed_m(p, b, h, qt)) {
+      run_keys<D, true, true>(p, smem, ln, b, h, qt, 0, tps, p.kv_valid, qop, acc_o, m_run, l_run);
+      for (int sg = 1; sg < p.n_kv_seg; ++sg) {
+        __syncthreads();   // every wave is done with the previous range's LDS tiles
+        const int kb = sg * seg_tiles;
+        run_keys<D, false, true>(p, smem, ln, b, h, qt, kb, kb + tps, sg * p.kv_seg_len + p.kv_valid, qop, acc_o,
+                                 m_run, l_run);
+      }
+    } else {
+      run_keys<D, true, false>(p, smem, ln, b, h, qt, 0, tps, p.kv_valid, qop, acc_o, m_run, l_run);
+      for (int sg = 1; sg < p.n_kv_seg; ++sg) {
+        __syncthreads();   // every wave is done with the previous range's LDS tiles
+        const int kb = sg * seg_tiles;
+        run_keys<D, false, false>(p, smem, ln, b, h, qt, kb, kb + tps, sg * p.kv_seg_len + p.kv_valid, qop, acc_o,
+                                  m_run, l_run);
+      }
     }
   } else {
 #pragma unroll

@@ -34,6 +34,24 @@ constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnBlockM = 32 * kAttnWaves;
 constexpr int kAttnBlockN = 64;
 
+// Fixed-m softmax: per-(b, h) key statistics over the real keys and the
+// per-row bound m_i = c2 * (q_i . kbar + |q_i| R), R = max_j |k_j - kbar|
+// (log2 units), plus a per-q-tile flag: 1 when every real row of the tile
+// has a bound spread 2 c2 |q_i| R small enough for the fixed maximum.
+constexpr int kStatRows = 256;   // key rows per statistics chunk
+struct FixedMParams {
+  const bf16_t *q, *k;
+  int64_t qs_b, qs_h, qs_s, ks_b, ks_h, ks_s;
+  int32_t B, H, d, s_q, s_kv, q_valid, kv_valid, q_seg_len, kv_seg_len;
+  int32_t n_chunks, n_real, n_qtiles;
+  float c2;
+  float *part;   // [B*H][n_chunks][d] partial key sums
+  float *kbar;   // [B*H][d] key mean
+  float *r2;     // [B*H][n_chunks] max |k_j - kbar|^2 of each chunk
+  float *m;      // [B*H][s_q] row bounds
+  int32_t *ok;   // [B*H][n_qtiles] fixed-m usable for the q-tile
+};
+
 // Parameters of the attention forward kernel (passed by value).
 struct AttnParams {
   const bf16_t *q, *k, *v;
@@ -57,6 +75,10 @@ struct AttnParams {
   float *sk_part_o;  // [q-tiles * sk_splits][kAttnThreads][d/2] partial O / l, fp32
   float *sk_part_l;  // [q-tiles * sk_splits][kAttnBlockM rows] partial LSE, log2 units
   int32_t *sk_count; // [q-tiles] arrival counters, zero on entry (left zero on exit)
+  // fixed-m softmax (fm_m != nullptr): row bounds [B*H][s_q] and per-q-tile
+  // flags [B*H][n_qtiles] from launch_fixed_m
+  const float *fm_m;
+  const int32_t *fm_ok;
 };
 
 // One tensor of the pre-pass: rows [0, rows) of x ((b, h, s) strides in
@@ -99,6 +121,7 @@ struct TableParams {
 
 // Launchers (host side, defined next to their kernels). Return hipError_t.
 hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream);
+hipError_t launch_fixed_m(const FixedMParams &p, hipStream_t stream);
 hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t stream);
 hipError_t launch_rope_rotate(const RopeRotateParams &p, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);

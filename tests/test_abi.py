@@ -83,6 +83,8 @@ def _desc(**kw):
     (dict(kv_seg_len=32, kv_valid=32), -2, b"key tile"),
     (dict(kv_seg_len=128, kv_valid=100, schedule=2), -2, b"balanced"),
     (dict(kv_seg_len=-1), -1, b"segment lengths"),
+    (dict(fixed_m=2), -1, b"fixed_m"),
+    (dict(fixed_m=1, schedule=2), -2, b"fixed-m"),
 ])
 def test_attn_fwd_rejects_bad_arguments_before_any_hip_call(L, kw, code, msg):
     d = _desc(**kw)

@@ -272,6 +272,84 @@ def test_segmented_edge_cases(ops, case):
     assert_pad_rows(og, lg, valid, "segmented edge")
 
 
+@pytest.mark.parametrize("name", ["wan480", "flux", "hunyuan"])
+def test_fixed_m_softmax_matches_oracle(ops, name):
+    """fixed_m = 1: the a-priori row-max bound (key mean + Cauchy-Schwarz over
+    the real keys) replaces the running maximum; graded at the bar against
+    the oracle, pad rows 0 / -inf, the same bits on a second call, and not
+    the online path's bits (so the fixed path ran)."""
+    import torch
+    w = W.WORKLOADS[name]
+    say(f"fixed-m {name}")
+    q, k, v = W.make_qkv(w)
+    pos = W.positions(w)
+    tabs = gpu_tables(ops, w)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    kw = dict(q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs)
+    o1, l1 = ops.attn_fwd(qd, kd, vd, fixed_m=True, **kw)
+    o2, l2 = ops.attn_fwd(qd, kd, vd, fixed_m=True, **kw)
+    o0, l0 = ops.attn_fwd(qd, kd, vd, **kw)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
+    valid = np.arange(w.s_pad) < w.s_valid
+    og, lg = to_np_f64(o1), to_np_f64(l1)
+    compare(og, lg, O_ref, L_ref, valid, f"fixed-m {name}")
+    assert_pad_rows(og, lg, valid, "fixed-m")
+    assert np.array_equal(raw_bits(o1), raw_bits(o2)) and np.array_equal(raw_bits(l1), raw_bits(l2))
+    assert not np.array_equal(raw_bits(l1), raw_bits(l0))
+
+
+def test_fixed_m_with_shifted_keys_segments_and_pads(ops):
+    """Keys with a large common mean (the bound is centred on it), two ring
+    segments with garbage pads (excluded from the key statistics: refilling
+    them with other garbage changes no bit), against the oracle."""
+    import torch
+    say("fixed-m: shifted keys, segments, pads")
+    r = np.random.default_rng(54)
+    L, per, S, d = 384, 330, 768, 128
+    q = W.bf16_bits((r.standard_normal((1, 3, S, d)) * 0.8).astype(np.float32))
+    mu = 2.0 * r.standard_normal(d)
+    k = W.bf16_bits((r.standard_normal((1, 3, S, d)) + mu).astype(np.float32))
+    v = W.bf16_bits(r.standard_normal((1, 3, S, d)).astype(np.float32))
+    valid = np.zeros(S, bool)
+    valid[oracle.segment_valid_rows(S, L, per)] = True
+    for x in (q, k, v):
+        x[:, :, ~valid] = W.finite_garbage_bits(r, x[:, :, ~valid].shape)
+    kw = dict(q_valid=per, kv_valid=per, q_seg_len=L, kv_seg_len=L, fixed_m=True)
+    o, l = ops.attn_fwd(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), **kw)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, ~valid] = W.finite_garbage_bits(r, k2[:, :, ~valid].shape)
+    v2[:, :, ~valid] = W.finite_garbage_bits(r, v2[:, :, ~valid].shape)
+    o2, l2 = ops.attn_fwd(to_dev_bf16(q), to_dev_bf16(k2), to_dev_bf16(v2), **kw)
+    torch.cuda.synchronize()
+    qf, kf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(k)
+    O_ref, L_ref = oracle.attention_segmented(qf, kf, oracle.bf16_to_f64(v), L, per, L, per)
+    og, lg = to_np_f64(o), to_np_f64(l)
+    bound = lse_rounding_bound(qf[:, :, valid], kf[:, :, valid], int(valid.sum()), 1.0 / math.sqrt(d))
+    lse_tol = np.full(L_ref.shape, 5e-3)
+    lse_tol[:, :, valid] = bound
+    compare(og, lg, O_ref, L_ref, valid, "fixed-m shifted keys", lse_tol=lse_tol)
+    assert_pad_rows(og, lg, valid, "fixed-m shifted keys")
+    assert np.array_equal(raw_bits(o2)[:, :, valid], raw_bits(o)[:, :, valid])
+    assert np.array_equal(raw_bits(l2)[:, :, valid], raw_bits(l)[:, :, valid])
+
+
+def test_fixed_m_falls_back_to_online_for_a_loose_bound(ops):
+    """Q x 8: the bound's spread exceeds the fixed-m limit on every q-tile, so
+    every q-tile keeps the online softmax: the same bits as fixed_m = 0."""
+    import torch
+    say("fixed-m fallback (Q x 8)")
+    r = np.random.default_rng(55)
+    q = W.bf16_bits((r.standard_normal((1, 2, 512, 128)) * 8.0).astype(np.float32))
+    k = W.bf16_bits(r.standard_normal((1, 2, 512, 128)).astype(np.float32))
+    v = W.bf16_bits(r.standard_normal((1, 2, 512, 128)).astype(np.float32))
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    o1, l1 = ops.attn_fwd(qd, kd, vd, q_valid=500, kv_valid=480, fixed_m=True)
+    o0, l0 = ops.attn_fwd(qd, kd, vd, q_valid=500, kv_valid=480)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_bits(o1), raw_bits(o0)) and np.array_equal(raw_bits(l1), raw_bits(l0))
+
+
 def test_short_kv_cross_attention(ops):
     """Video queries over 512 text keys (no RoPE): the short-KV regime of the
     Wan cross-attention (maxdiffusion PR #491, fused short-KV cross-attention
