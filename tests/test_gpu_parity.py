@@ -350,6 +350,81 @@ def test_fixed_m_falls_back_to_online_for_a_loose_bound(ops):
     assert np.array_equal(raw_bits(o1), raw_bits(o0)) and np.array_equal(raw_bits(l1), raw_bits(l0))
 
 
+def _random_case(seed):
+    r = np.random.default_rng(seed)
+    d = int(r.choice([64, 128]))
+    s_q, s_kv = int(r.integers(1, 700)), int(r.integers(1, 700))
+    c = dict(B=int(r.integers(1, 3)), H=int(r.integers(1, 5)), d=d, s_q=s_q, s_kv=s_kv,
+             q_valid=int(r.integers(0, s_q + 1)), kv_valid=int(r.integers(0, s_kv + 1)),
+             rope_q=bool(r.random() < 0.6), rope_k=bool(r.random() < 0.6), norm=bool(r.random() < 0.3),
+             tok_layout=bool(r.random() < 0.5), f32_out=bool(r.random() < 0.3),
+             schedule=int(r.choice([0, 1, 2])), scale=float(r.choice([0.0, 0.05])))
+    c["fixed_m"] = bool(c["schedule"] != 2 and r.random() < 0.4)
+    return c
+
+
+@pytest.mark.parametrize("seed", list(range(60, 72)))
+def test_random_shapes_against_oracle(ops, seed):
+    """Seeded random shapes and options (ragged lengths including 0, d 64 /
+    128, dense or token-major strides, RoPE on Q and / or K, fused norm,
+    fp32 output, every schedule, fixed-m, an explicit scale) against the
+    oracle: O within the derived rounding bound of the oracle on the
+    bf16-rounded prepared Q/K, LSE within the derived bound of the unrounded
+    oracle, pad rows 0 / -inf."""
+    import torch
+    c = _random_case(seed)
+    say(f"random {seed}: {c}")
+    r = np.random.default_rng(1000 + seed)
+    B, H, d, s_q, s_kv = c["B"], c["H"], c["d"], c["s_q"], c["s_kv"]
+    q = W.bf16_bits(r.standard_normal((B, H, s_q, d)).astype(np.float32))
+    k = W.bf16_bits(r.standard_normal((B, H, s_kv, d)).astype(np.float32))
+    v = W.bf16_bits(r.standard_normal((B, H, s_kv, d)).astype(np.float32))
+    k[:, :, c["kv_valid"]:] = W.finite_garbage_bits(r, k[:, :, c["kv_valid"]:].shape)
+    v[:, :, c["kv_valid"]:] = W.finite_garbage_bits(r, v[:, :, c["kv_valid"]:].shape)
+    pq = r.integers(0, 100, (s_q, 1)).astype(np.int32)
+    pk = r.integers(0, 100, (s_kv, 1)).astype(np.int32)
+    wq = (1.0 + 0.2 * r.standard_normal(d)).astype(np.float32)
+    wk = (1.0 + 0.2 * r.standard_normal(d)).astype(np.float32)
+
+    def dev_in(x):
+        t = to_dev_bf16(x)
+        return t.transpose(1, 2).contiguous().transpose(1, 2) if c["tok_layout"] else t
+
+    tq = ops.rope_split_tables(torch.from_numpy(pq).to(dev()), (d,), d, 10000.0) if c["rope_q"] else None
+    tk = ops.rope_split_tables(torch.from_numpy(pk).to(dev()), (d,), d, 10000.0) if c["rope_k"] else None
+    nq = torch.from_numpy(wq).to(dev()) if c["norm"] else None
+    nk = torch.from_numpy(wk).to(dev()) if c["norm"] else None
+    o, l = ops.attn_fwd(dev_in(q), dev_in(k), dev_in(v), q_valid=c["q_valid"], kv_valid=c["kv_valid"],
+                        rope_q=tq, rope_k=tk, q_norm=nq, k_norm=nk, sm_scale=c["scale"],
+                        out_dtype=torch.float32 if c["f32_out"] else torch.bfloat16,
+                        schedule=c["schedule"], fixed_m=c["fixed_m"])
+    torch.cuda.synchronize()
+    qf, kf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(k)
+    if c["norm"]:
+        qf, kf = oracle.rms_norm(qf, wq, 1e-6), oracle.rms_norm(kf, wk, 1e-6)
+    if c["rope_q"]:
+        qf = oracle.rope_split_halves(qf, *oracle.rope_tables(pq, (d,), 10000.0))
+    if c["rope_k"]:
+        kf = oracle.rope_split_halves(kf, *oracle.rope_tables(pk, (d,), 10000.0))
+    scale = c["scale"] or 1.0 / math.sqrt(d)
+    vf = oracle.bf16_to_f64(v)
+    O_ref, L_ref = oracle.attention(qf, kf, vf, c["q_valid"], c["kv_valid"], scale=scale)
+    prepared = c["norm"] or c["rope_q"] or c["rope_k"]
+    rb = (lambda x: oracle.bf16_to_f64(W.bf16_bits(x.astype(np.float32)))) if prepared else (lambda x: x)
+    O_rr, L_rr = oracle.attention(rb(qf), rb(kf), vf, c["q_valid"], c["kv_valid"], scale=scale)
+    og, lg = to_np_f64(o), to_np_f64(l)
+    valid = np.arange(s_q) < c["q_valid"]
+    assert_pad_rows(og, lg, valid if c["kv_valid"] > 0 else np.zeros(s_q, bool), f"random {seed}")
+    if c["kv_valid"] == 0 or c["q_valid"] == 0:
+        return
+    otol = o_rounding_bound(O_rr, vf[:, :, :c["kv_valid"]])
+    do = np.abs(og - O_rr)[:, :, valid]
+    assert (do <= otol[:, :, valid]).all(), (seed, float((do / otol[:, :, valid]).max()))
+    bound = lse_rounding_bound(qf, kf, c["kv_valid"], scale)
+    dl = np.abs(lg - L_ref)[:, :, valid]
+    assert np.isfinite(lg[:, :, valid]).all() and (dl <= np.maximum(bound[:, :, valid], 1e-5)).all(), seed
+
+
 def test_short_kv_cross_attention(ops):
     """Video queries over 512 text keys (no RoPE): the short-KV regime of the
     Wan cross-attention (maxdiffusion PR #491, fused short-KV cross-attention
