@@ -1,9 +1,10 @@
 """Benchmark of the DiT self-attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic tokens:
-  RoPE tables from positions -> tail pad of Q, K, V tokens ([B, S, H, d]) ->
-  attention forward (Q / K rotation pre-pass + the attention kernel, pad
-  keys masked) -> unpad of O.
+  RoPE tables from positions -> tail pad of the fused QKV tokens
+  ([B, S, 3, H, d], one call) -> attention forward on the strided Q, K, V
+  views (Q / K rotation pre-pass + the attention kernel, pad keys masked)
+  -> unpad of O.
 Inputs are resident in HBM before timing starts. Throughput is counted over
 valid tokens: FLOP = 4 * B * H * S_valid^2 * d per step.
 
@@ -62,6 +63,29 @@ def kernel_source_hash() -> str:
 
 
 # ---------------------------------------------------------------- helpers
+def sclk_levels():
+    """Shader-clock DPM levels of each amdgpu card in sysfs (MHz); `current`
+    holds the level(s) the driver marks active. None where sysfs hides them."""
+    import re
+    out = []
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))[:16]:
+        try:
+            with open(f) as fh:
+                txt = fh.read()
+        except OSError:
+            continue
+        lv = re.findall(r"(\d+)\s*[Mm][Hh]z(\s*\*)?", txt)
+        out.append({"card": f.split("/")[4], "levels_mhz": [int(a) for a, _ in lv],
+                    "current_mhz": [int(a) for a, star in lv if star.strip()]})
+    return out or None
+
+
+def device_info(torch, sclk_busy):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "sclk_during_timed_steps": sclk_busy, "sclk_after": sclk_levels()}
+
+
 def dev_tensors(w, np, torch, dev):
     import workloads as W
     q, k, v = W.make_qkv(w)
@@ -346,21 +370,24 @@ def main():
 
     (q, k, v), _ = dev_tensors(w, np, torch, torch.device("cpu"))
 
-    # token-major inputs [B, S_valid, H, d] (what an all-to-all hands over)
+    # token-major fused QKV [B, S_valid, 3, H, d]: what one all-to-all of the
+    # stacked Q, K, V hands over (sequence shard -> head shard)
     def tok(x):
         t = torch.from_numpy(np.ascontiguousarray(x[:, :, :Sv].transpose(0, 2, 1, 3)).view(np.int16))
-        return t.view(torch.bfloat16).to(dev)
-    q_tok, k_tok, v_tok = tok(q), tok(k), tok(v)
+        return t.view(torch.bfloat16)
+    qkv_tok = torch.stack([tok(q), tok(k), tok(v)], dim=2).to(dev)
+    q_tok = qkv_tok[:, :, 0].contiguous()   # one tensor's worth, for the single-tensor pad figure
     pos = torch.from_numpy(W.positions(w)).to(dev)
+    qkvp = torch.empty((B, Sp, 3, H, d), dtype=torch.bfloat16, device=dev)
     qp = torch.empty((B, Sp, H, d), dtype=torch.bfloat16, device=dev)
-    kp, vp, op = torch.empty_like(qp), torch.empty_like(qp), torch.empty_like(qp)
+    op = torch.empty_like(qp)
     o_tok = torch.empty_like(q_tok)
     lse = torch.empty((B, H, Sp), dtype=torch.float32, device=dev)
     cos = torch.empty((Sp, d // 2), dtype=torch.float32, device=dev)
     sin = torch.empty_like(cos)
     L = ops._native.lib()
     chans = (ctypes.c_int32 * len(w.axes))(*w.axes)
-    qv, kv_, vv = qp.transpose(1, 2), kp.transpose(1, 2), vp.transpose(1, 2)
+    qv, kv_, vv = (qkvp[:, :, i].transpose(1, 2) for i in range(3))   # [B, H, S_pad, d] views
     ws = torch.empty(ops.attn_workspace_size(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin)),
                      dtype=torch.uint8, device=dev)
 
@@ -369,9 +396,7 @@ def main():
         ops._native.check(L.dit_rope_split_tables(ctypes.c_void_p(pos.data_ptr()), Sp, len(w.axes), chans, d,
                                                   float(w.theta), ctypes.c_void_p(cos.data_ptr()),
                                                   ctypes.c_void_p(sin.data_ptr()), s), "tables")
-        ops.pad_tokens(q_tok, Sp, out=qp)
-        ops.pad_tokens(k_tok, Sp, out=kp)
-        ops.pad_tokens(v_tok, Sp, out=vp)
+        ops.pad_tokens(qkv_tok, Sp, out=qkvp)
         ops.attn_fwd(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin),
                      out=op.transpose(1, 2), lse=lse, workspace=ws)
         ops.unpad_tokens(op, Sv, out=o_tok)
@@ -384,6 +409,7 @@ def main():
     for _ in range(args.steps):
         step()
     e1.record()
+    sclk_busy = sclk_levels()   # read while the queued steps still run
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
@@ -404,6 +430,7 @@ def main():
         ctypes.c_void_p(pos.data_ptr()), Sp, len(w.axes), chans, d, float(w.theta), ctypes.c_void_p(cos.data_ptr()),
         ctypes.c_void_p(sin.data_ptr()), ops._stream(dev)), "tables"), n)
     us_pad = time_us(torch, lambda: ops.pad_tokens(q_tok, Sp, out=qp), n)
+    us_pad_qkv = time_us(torch, lambda: ops.pad_tokens(qkv_tok, Sp, out=qkvp), n)
     us_unpad = time_us(torch, lambda: ops.unpad_tokens(op, Sv, out=o_tok), n)
     us_call = time_us(torch, lambda: ops.attn_fwd(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin),
                                                   rope_k=(cos, sin), out=op.transpose(1, 2), lse=lse,
@@ -428,17 +455,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "B": B, "H": H, "d": d, "s_valid": Sv, "s_pad": Sp,
                    "flop_per_step": flop,
-                   "step": "tables + pad(Q,K,V) + attn_fwd(Q/K RoPE pre-pass + attention kernel) + unpad(O)"},
+                   "step": "tables + pad(fused QKV [B,S,3,H,d]) + attn_fwd(Q/K RoPE pre-pass + attention "
+                           "kernel on the strided Q/K/V views) + unpad(O)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch", "traffic_source": traffic_src,
                      "algorithmic_flop_per_launch": flop, "kernel": "attn_fwd_kernel<128, false>",
                      "kernel_us": us_attn},
         "kernels_us": {"attn_fwd_kernel": us_attn, "dit_attn_fwd_call(Q/K pre-pass + kernel)": us_call,
-                       "rope_tables": us_tables, "pad_tokens(one tensor)": us_pad, "unpad_tokens": us_unpad,
+                       "rope_tables": us_tables, "pad_tokens(one tensor)": us_pad,
+                       "pad_tokens(fused QKV)": us_pad_qkv, "unpad_tokens": us_unpad,
                        "pad_GBps": pad_bytes / (us_pad * 1e-6) / 1e9,
+                       "pad_qkv_GBps": 3 * pad_bytes / (us_pad_qkv * 1e-6) / 1e9,
                        "unpad_GBps": 2 * Sv * H * d * 2 * B / (us_unpad * 1e-6) / 1e9},
         "pct_of_peak_step": flop / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS * 100,
+        "device": device_info(torch, sclk_busy),
     }
     del k_rot
     if not args.no_configs:

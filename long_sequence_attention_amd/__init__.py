@@ -39,6 +39,20 @@ def _need_cuda(name, t, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _same_device(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _check_out(name, t, shape, dtypes, dev):
+    """A caller-provided output: on dev, one of dtypes, exactly shape, dense."""
+    _need_cuda(name, t)
+    if t.dtype not in dtypes or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{name} must be a dense {' or '.join(str(x) for x in dtypes)} tensor of shape "
+                         f"{tuple(shape)} on {dev}; got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
 def _strides4(name, t):
     if t.dim() != 4:
         raise ValueError(f"{name} must be 4-D [B, H, S, d] (any layout with d contiguous)")
@@ -113,6 +127,9 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_cuda(name, t, torch.bfloat16)
+    _same_device(q.device, k=k, v=v, out=out, lse=lse, workspace=workspace, q_norm=q_norm, k_norm=k_norm,
+                 cos_q=None if rope_q is None else rope_q[0], sin_q=None if rope_q is None else rope_q[1],
+                 cos_k=None if rope_k is None else rope_k[0], sin_k=None if rope_k is None else rope_k[1])
     B, H, s_q, d = q.shape
     if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
@@ -149,6 +166,9 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
     if need.value:
         if workspace is None:
             workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        _need_cuda("workspace", workspace)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be a dense tensor")
         if workspace.numel() * workspace.element_size() < need.value:
             raise ValueError(f"workspace needs {need.value} bytes")
         desc.workspace = workspace.data_ptr()
@@ -179,10 +199,16 @@ def lse_merge(o_parts, lse_parts, *, q_valid=None, out_dtype=torch.bfloat16, out
             raise ValueError("LSE parts must be dense fp32 [B, H, S]")
     q_valid = S if q_valid is None else int(q_valid)
     dev = o_parts[0].device
+    _same_device(dev, **{f"o_part{i}": o for i, o in enumerate(o_parts)},
+                 **{f"lse_part{i}": l for i, l in enumerate(lse_parts)})
     if out is None:
         out = torch.empty((B, H, S, d), dtype=out_dtype, device=dev)
+    else:
+        _check_out("out", out, (B, H, S, d), (torch.bfloat16, torch.float32), dev)
     if lse_out is None and return_lse:
         lse_out = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    elif lse_out is not None:
+        _check_out("lse_out", lse_out, (B, H, S), (torch.float32,), dev)
     optr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in o_parts])
     lptr = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
     rc = N.lib().dit_lse_merge(n, optr, lptr, N.DIT_F32 if pdt == torch.float32 else N.DIT_BF16,
@@ -219,6 +245,8 @@ def pad_tokens(x, s_pad: int, out=None):
     row_bytes = x.element_size() * math.prod(x.shape[2:])
     if out is None:
         out = torch.empty((B, s_pad) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
+    else:
+        _check_out("out", out, (B, int(s_pad)) + tuple(x.shape[2:]), (x.dtype,), x.device)
     N.check(N.lib().dit_pad_tokens(_ptr(x), _ptr(out), B, s_valid, int(s_pad), row_bytes, _stream(x.device)),
             "pad_tokens")
     return out
@@ -233,6 +261,8 @@ def unpad_tokens(x, s_valid: int, out=None):
     row_bytes = x.element_size() * math.prod(x.shape[2:])
     if out is None:
         out = torch.empty((B, int(s_valid)) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
+    else:
+        _check_out("out", out, (B, int(s_valid)) + tuple(x.shape[2:]), (x.dtype,), x.device)
     N.check(N.lib().dit_unpad_tokens(_ptr(x), _ptr(out), B, s_pad, int(s_valid), row_bytes, _stream(x.device)),
             "unpad_tokens")
     return out

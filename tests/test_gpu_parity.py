@@ -686,6 +686,36 @@ def test_no_valid_keys_gives_zero_and_minus_inf(ops):
     assert (to_np_f64(o) == 0).all() and np.isneginf(to_np_f64(l)).all()
 
 
+def test_binding_rejects_bad_caller_buffers(ops):
+    """Caller-provided outputs of the wrong shape, dtype or layout, and
+    operands on the wrong device, raise ValueError before any launch."""
+    import torch
+    say("binding checks")
+    x = torch.zeros((1, 37, 3), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(ValueError):
+        ops.pad_tokens(x, 48, out=torch.empty((1, 47, 3), dtype=torch.bfloat16, device=dev()))
+    with pytest.raises(ValueError):
+        ops.pad_tokens(x, 48, out=torch.empty((1, 48, 3), dtype=torch.float32, device=dev()))
+    with pytest.raises(ValueError):
+        ops.unpad_tokens(torch.zeros((1, 48, 3), dtype=torch.bfloat16, device=dev()), 37,
+                         out=torch.empty((1, 3, 48), dtype=torch.bfloat16, device=dev()).transpose(1, 2)[:, :37])
+    po = [torch.zeros((1, 2, 64, 64), dtype=torch.float32, device=dev()) for _ in range(2)]
+    pl = [torch.zeros((1, 2, 64), dtype=torch.float32, device=dev()) for _ in range(2)]
+    with pytest.raises(ValueError):
+        ops.lse_merge(po, pl, out=torch.empty((1, 2, 63, 64), dtype=torch.bfloat16, device=dev()))
+    with pytest.raises(ValueError):
+        ops.lse_merge(po, pl, lse_out=torch.empty((1, 2, 64), dtype=torch.bfloat16, device=dev()))
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(ValueError):
+        ops.attn_fwd(q, q, q, lse=torch.empty((1, 2, 64), dtype=torch.float32))            # host LSE
+    with pytest.raises(ValueError):
+        ops.attn_fwd(q, q, q, out=torch.empty((1, 2, 64, 32), dtype=torch.bfloat16, device=dev()))
+    tabs = (torch.ones((64, 32), device=dev()), torch.zeros((64, 32), device=dev()))
+    with pytest.raises(ValueError):   # too small a workspace
+        ops.attn_fwd(q, q, q, rope_q=tabs, rope_k=tabs, workspace=torch.empty(16, dtype=torch.uint8, device=dev()))
+    torch.cuda.synchronize()
+
+
 def test_pad_unpad_round_trip(ops):
     import torch
     say("pad/unpad")
