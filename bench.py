@@ -276,6 +276,15 @@ def config_table(np, torch, ops, W, dev, n_iter):
                                                  rope_q=tabs, rope_k=tabs, out=o, lse=lse,
                                                  workspace=ws), n, warm_s=0.3)
         ent = {"us": us, "tflops": w.valid_flop / us / 1e6, "pct_peak": w.valid_flop / us / 1e6 / PEAK_BF16_TFLOPS * 100}
+        if w.rope and w.valid_flop < 1e12:   # the kernel alone, on the Q / K the pre-pass left in the workspace
+            n_el = w.B * w.H * w.s_pad * w.d
+            k_rot = ws[: n_el * 2].view(torch.bfloat16).view(w.B, w.H, w.s_pad, w.d).clone()
+            q_rot = ws[n_el * 2: n_el * 4].view(torch.bfloat16).view(w.B, w.H, w.s_pad, w.d).clone()
+            kus = time_us(torch, lambda: ops.attn_fwd(q_rot, k_rot, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
+                                                      out=o, lse=lse), n, warm_s=0.3)
+            ent.update({"kernel_us": kus, "kernel_pct_peak": w.valid_flop / kus / 1e6 / PEAK_BF16_TFLOPS * 100,
+                        "prepass_us": us - kus})
+            del k_rot, q_rot
         if name in ("wan480", "hunyuan", "wan720"):   # the fixed-m softmax (key / query statistics passes)
             wsf = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
                                                           rope_q=tabs, rope_k=tabs, fixed_m=True), 256),

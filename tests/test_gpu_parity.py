@@ -96,6 +96,41 @@ def test_parity_full_config(ops, name):
     assert_pad_rows(og, lg, valid, name)
 
 
+def test_wan480_in_the_bench_step_layout(ops):
+    """The Wan 480p step exactly as the benchmark runs it: the real tokens as
+    one token-major QKV tensor [B, S_valid, 3, H, d], one tail pad to
+    S_pad, tables from positions, attention on the strided Q, K, V views of
+    the padded buffer with a caller workspace and O written into a
+    token-major [B, S_pad, H, d] buffer, then the unpad. Graded against the
+    oracle, and bit-identical to the dense-layout call on the workload's
+    garbage-padded tensors (pad rows never reach a valid output)."""
+    import torch
+    w = W.WORKLOADS["wan480"]
+    say("wan480 in the bench step layout (fused QKV, strided views)")
+    B, H, d, Sv, Sp = w.B, w.H, w.d, w.s_valid, w.s_pad
+    q, k, v = W.make_qkv(w)
+    tok = lambda x: np.ascontiguousarray(x[:, :, :Sv].transpose(0, 2, 1, 3))
+    qkv_tok = to_dev_bf16(np.stack([tok(q), tok(k), tok(v)], axis=2))
+    cos, sin = ops.rope_split_tables(torch.from_numpy(W.positions(w)).to(dev()), w.axes, d, w.theta)
+    qkvp = ops.pad_tokens(qkv_tok, Sp)
+    qv, kv_, vv = (qkvp[:, :, i].transpose(1, 2) for i in range(3))
+    ws = torch.empty(ops.attn_workspace_size(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin),
+                                             rope_k=(cos, sin)), dtype=torch.uint8, device=dev())
+    op = torch.empty((B, Sp, H, d), dtype=torch.bfloat16, device=dev())
+    lse = torch.empty((B, H, Sp), dtype=torch.float32, device=dev())
+    ops.attn_fwd(qv, kv_, vv, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin),
+                 out=op.transpose(1, 2), lse=lse, workspace=ws)
+    o_tok = ops.unpad_tokens(op, Sv)
+    o_dense, l_dense = run_gpu(ops, w, q, k, v, (cos, sin))
+    torch.cuda.synchronize()
+    assert torch.equal(o_tok.transpose(1, 2).contiguous().view(torch.int16), o_dense[:, :, :Sv].view(torch.int16))
+    assert torch.equal(lse, l_dense)
+    pos = W.positions(w)
+    O_ref, L_ref = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, Sv, Sv)
+    og = to_np_f64(o_tok).transpose(0, 2, 1, 3)
+    compare(og, to_np_f64(lse)[:, :, :Sv], O_ref[:, :, :Sv], L_ref[:, :, :Sv], np.ones(Sv, bool), "bench layout")
+
+
 def _raw_qk_with_row_scales(w, seed):
     """Q/K draws of a workload without its RMS normalisation, each row scaled
     by exp(N(0, 0.5^2)) and Q by 3 overall, rounded to bf16: inputs on which
