@@ -83,7 +83,8 @@ def sclk_levels():
 def device_info(torch, sclk_busy):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
-            "sclk_during_timed_steps": sclk_busy, "sclk_after": sclk_levels()}
+            "sclk_during_timed_steps": sclk_busy, "sclk_after": sclk_levels(),
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
 
 
 def dev_tensors(w, np, torch, dev):
@@ -128,12 +129,26 @@ def cpu_baseline(w, q, k, v):
     walls = []
     for _ in range(3):
         t0 = time.perf_counter()
-        oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
+        ref = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
         walls.append(time.perf_counter() - t0)
     dt = min(walls)
     return {"value": w.valid_flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"full {w.name} workload (B={w.B}, H={w.H}, all {w.s_valid} valid query rows, RoPE tables, "
-                      f"RoPE, attention, LSE), NumPy float64, best of 3: {dt:.2f} s wall"}
+                      f"RoPE, attention, LSE), NumPy float64, best of 3: {dt:.2f} s wall"}, ref
+
+
+def parity_of_step(np, o_tok, lse, ref, s_valid):
+    """The last timed step's O ([B, S_valid, H, d]) and LSE against the
+    oracle's result on the same inputs, with the acceptance bar."""
+    O_ref, L_ref = ref
+    og = o_tok.float().cpu().numpy().astype(np.float64).transpose(0, 2, 1, 3)
+    lg = lse[:, :, :s_valid].cpu().numpy().astype(np.float64)
+    do = np.abs(og - O_ref[:, :, :s_valid])
+    dl = np.abs(lg - L_ref[:, :, :s_valid])
+    res = {"o_max_abs": float(do.max()), "o_mean_abs": float(do.mean()), "lse_max_abs": float(dl.max()),
+           "bar": {"o_max_abs": 1.5e-2, "o_mean_abs": 2e-3, "lse_max_abs": 5e-3}}
+    res["pass"] = bool(res["o_max_abs"] <= 1.5e-2 and res["o_mean_abs"] <= 2e-3 and res["lse_max_abs"] <= 5e-3)
+    return res
 
 
 def read_traffic():
@@ -484,7 +499,8 @@ def main():
     if not args.no_configs:
         out["configs_attn_fwd"] = config_table(np, torch, ops, W, dev, n)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v)
+        out["cpu_baseline"], ref = cpu_baseline(w, q, k, v)
+        out["step_parity_vs_oracle"] = parity_of_step(np, o_tok, lse, ref, Sv)
     print(json.dumps(out), flush=True)
 
 
