@@ -214,15 +214,29 @@ def hbm_passes(args):
     lm = torch.empty((1, H, Sp), dtype=torch.float32, device=dev)
     pos = torch.from_numpy(W.positions(w)).to(dev)
     row = H * d * 2
+    # a full attention call on token-major random inputs, for the Q / K
+    # rotation pre-pass's duration in a kernel trace (its bytes: Q and K rows
+    # read and written, plus the fp32 tables once per row and group of four heads)
+    cos, sin = ops.rope_split_tables(pos, w.axes, d, w.theta)
+    qa, ka, va = (torch.randn((1, Sp, H, d), device=dev).to(torch.bfloat16).transpose(1, 2) for _ in range(3))
+    oa = torch.empty((1, Sp, H, d), dtype=torch.bfloat16, device=dev).transpose(1, 2)
+    ws = torch.empty(ops.attn_workspace_size(qa, ka, va, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin)),
+                     dtype=torch.uint8, device=dev)
+    groups = -(-H // 4)
+    prepass_bytes = (Sp + Sv) * row * 2 + (Sp + Sv) * groups * d * 4
     res = {}
     for name, fn, nbytes in (
             ("pad_tokens", lambda: ops.pad_tokens(x, Sp, out=xp), (Sv + Sp) * row),
             ("unpad_tokens", lambda: ops.unpad_tokens(xp, Sv, out=xu), 2 * Sv * row),
             ("lse_merge_4xf32_to_bf16", lambda: ops.lse_merge(parts_o, parts_l, q_valid=Sv, out=om, lse_out=lm),
              4 * H * Sp * (d * 4 + 4) + H * Sp * (d * 2 + 4)),
-            ("rope_split_tables", lambda: ops.rope_split_tables(pos, w.axes, d, w.theta), Sp * d // 2 * 8)):
-        us = time_us(torch, fn, 20, warm=5)
-        res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / us / 1e3}
+            ("rope_split_tables", lambda: ops.rope_split_tables(pos, w.axes, d, w.theta), Sp * d // 2 * 8),
+            ("attn_fwd_call(pre-pass + attention kernel)", lambda: ops.attn_fwd(
+                qa, ka, va, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin), out=oa, workspace=ws),
+             None)):
+        us = time_us(torch, fn, 20 if nbytes else 3, warm=5 if nbytes else 1)
+        res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / us / 1e3} if nbytes else {"us": us}
+    res["prepass_algorithmic_bytes"] = prepass_bytes
     print(json.dumps({"hbm_passes_wan720": res}), flush=True)
 
 
