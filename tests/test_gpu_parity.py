@@ -460,6 +460,71 @@ def test_random_shapes_against_oracle(ops, seed):
     assert np.isfinite(lg[:, :, valid]).all() and (dl <= np.maximum(bound[:, :, valid], 1e-5)).all(), seed
 
 
+def _random_segment_case(seed):
+    r = np.random.default_rng(seed)
+    kl = 64 * int(r.integers(1, 6))
+    ql = 64 * int(r.integers(1, 6))
+    c = dict(B=int(r.integers(1, 3)), H=int(r.integers(1, 4)), d=int(r.choice([64, 128])),
+             n_kseg=int(r.integers(1, 4)), kv_seg_len=kl, kv_valid=int(r.integers(1, kl + 1)),
+             n_qseg=int(r.integers(1, 4)), q_seg_len=ql, q_valid=int(r.integers(0, ql + 1)),
+             rope_q=bool(r.random() < 0.6), rope_k=bool(r.random() < 0.6), fixed_m=bool(r.random() < 0.4))
+    return c
+
+
+@pytest.mark.parametrize("seed", list(range(80, 88)))
+def test_random_segmented_against_oracle(ops, seed):
+    """Seeded random ring layouts: 1-3 key segments and 1-3 query segments of
+    64-multiple lengths, each padded at its own tail with garbage, d 64 /
+    128, RoPE on Q and / or K, online or fixed-m softmax; against the
+    oracle's segmented attention on the bf16-rounded prepared Q/K (O within
+    the derived bound, LSE within the derived bound of the unrounded
+    oracle); pad rows 0 / -inf."""
+    import torch
+    c = _random_segment_case(seed)
+    say(f"random segmented {seed}: {c}")
+    r = np.random.default_rng(2000 + seed)
+    B, H, d = c["B"], c["H"], c["d"]
+    s_q, s_kv = c["n_qseg"] * c["q_seg_len"], c["n_kseg"] * c["kv_seg_len"]
+    qrows = oracle.segment_valid_rows(s_q, c["q_seg_len"], c["q_valid"])
+    krows = oracle.segment_valid_rows(s_kv, c["kv_seg_len"], c["kv_valid"])
+    q = W.finite_garbage_bits(r, (B, H, s_q, d))
+    k = W.finite_garbage_bits(r, (B, H, s_kv, d))
+    v = W.finite_garbage_bits(r, (B, H, s_kv, d))
+    q[:, :, qrows] = W.bf16_bits(r.standard_normal((B, H, len(qrows), d)).astype(np.float32))
+    k[:, :, krows] = W.bf16_bits(r.standard_normal((B, H, len(krows), d)).astype(np.float32))
+    v[:, :, krows] = W.bf16_bits(r.standard_normal((B, H, len(krows), d)).astype(np.float32))
+    pq = np.zeros((s_q, 1), np.int32)
+    pk = np.zeros((s_kv, 1), np.int32)
+    pq[qrows, 0] = r.integers(0, 200, len(qrows))
+    pk[krows, 0] = r.integers(0, 200, len(krows))
+    tq = ops.rope_split_tables(torch.from_numpy(pq).to(dev()), (d,), d, 10000.0) if c["rope_q"] else None
+    tk = ops.rope_split_tables(torch.from_numpy(pk).to(dev()), (d,), d, 10000.0) if c["rope_k"] else None
+    o, l = ops.attn_fwd(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), q_valid=c["q_valid"],
+                        kv_valid=c["kv_valid"], q_seg_len=c["q_seg_len"], kv_seg_len=c["kv_seg_len"],
+                        rope_q=tq, rope_k=tk, fixed_m=c["fixed_m"])
+    torch.cuda.synchronize()
+    qf, kf, vf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(k), oracle.bf16_to_f64(v)
+    if c["rope_q"]:
+        qf = oracle.rope_split_halves(qf, *oracle.rope_tables(pq, (d,), 10000.0))
+    if c["rope_k"]:
+        kf = oracle.rope_split_halves(kf, *oracle.rope_tables(pk, (d,), 10000.0))
+    seg = (c["q_seg_len"], c["q_valid"], c["kv_seg_len"], c["kv_valid"])
+    O_ref, L_ref = oracle.attention_segmented(qf, kf, vf, *seg)
+    rb = lambda x: oracle.bf16_to_f64(W.bf16_bits(x.astype(np.float32)))
+    O_rr, _ = oracle.attention_segmented(rb(qf), rb(kf), vf, *seg)
+    og, lg = to_np_f64(o), to_np_f64(l)
+    valid = np.zeros(s_q, bool)
+    valid[qrows] = True
+    assert_pad_rows(og, lg, valid, f"random segmented {seed}")
+    if not valid.any():
+        return
+    otol = o_rounding_bound(O_rr, vf[:, :, krows])
+    assert (np.abs(og - O_rr)[:, :, valid] <= otol[:, :, valid]).all(), seed
+    bound = lse_rounding_bound(qf[:, :, qrows], kf[:, :, krows], len(krows), 1.0 / math.sqrt(d))
+    dl = np.abs(lg - L_ref)[:, :, valid]
+    assert np.isfinite(lg[:, :, valid]).all() and (dl <= bound).all(), seed
+
+
 def test_short_kv_cross_attention(ops):
     """Video queries over 512 text keys (no RoPE): the short-KV regime of the
     Wan cross-attention (maxdiffusion PR #491, fused short-KV cross-attention
