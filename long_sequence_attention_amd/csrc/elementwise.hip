@@ -141,8 +141,8 @@ hipError_t launch_rope_tables(const TableParams &p, hipStream_t stream) {
 // four granules per thread on at most 4096 blocks; larger ones stream one
 // granule per thread on up to 32768 blocks with non-temporal source loads
 // (measured on MI355X: 6.8 TB/s against 4.8 TB/s for the small-copy form
-// on a 387 MB pad, while the small-copy form makes the Wan 480p step, with
-// its three pads and one unpad of 24 MB each, about 1 us faster).
+// on a 387 MB pad, while the small-copy form makes the Wan 480p step, whose
+// pad and unpad move 24-73 MB each, about 1 us faster).
 template <typename V>
 static void launch_copy_v(const void *in, void *out, int B, int s_in, int s_out, int n_copy, int64_t row_bytes,
                           hipStream_t stream) {
