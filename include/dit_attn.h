@@ -100,9 +100,9 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  *
  * workspace: device scratch for the once-per-call rotated (and normalised)
  * copies of K and Q (dense bf16 [B, H, s, d] each, when their tables or norm
- * weights are given) and, under the
- * BALANCED schedule, the partial results of split query tiles and their
- * arrival counters. Required (non-NULL, 256-byte aligned, at least
+ * weights are given), under the BALANCED schedule the partial results of
+ * split query tiles and their arrival counters, and with fixed_m the key
+ * and query statistics (fp32, about B*H*(s_q + 2*d + s_kv*d/256) values). Required (non-NULL, 256-byte aligned, at least
  * dit_attn_workspace_size() bytes) when that size is non-zero. The caller
  * owns it; its contents need not be initialised. Calls that share one
  * workspace must not overlap.
@@ -162,9 +162,10 @@ typedef struct dit_attn_desc {
   int32_t fixed_m;               /* 0 = online softmax, 1 = fixed-m: see above */
 } dit_attn_desc;
 
-/* Bytes of workspace dit_attn_fwd needs for `desc` (0 when K is not rotated
- * and the schedule needs no partial results). Under BALANCED the size depends
- * on the current device's compute-unit count (DIT_ERR_HIP if it cannot be
+/* Bytes of workspace dit_attn_fwd needs for `desc` (0 when neither Q nor K
+ * is rotated or normalised, the schedule needs no partial results and
+ * fixed_m is 0, or when kv_valid is 0). Under BALANCED the size depends on
+ * the current device's compute-unit count (DIT_ERR_HIP if it cannot be
  * queried). */
 DIT_API int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes);
 
