@@ -392,8 +392,9 @@ int dit_rope_split_tables(const int32_t *pos, int S, int n_axes, const int32_t *
   if ((int64_t)S * (d / 2) > 0x7fffffffLL) return fail(DIT_ERR_UNSUPPORTED, "S * d/2 must be below 2^31");
   int sum = 0;
   for (int a = 0; a < n_axes; ++a) {
-    if (axis_channels[a] <= 0 || axis_channels[a] % 2)
-      return fail(DIT_ERR_INVALID, "axis %d has %d channels: each axis needs a positive even count", a, axis_channels[a]);
+    if (axis_channels[a] <= 0 || axis_channels[a] % 2 || axis_channels[a] > d)
+      return fail(DIT_ERR_INVALID, "axis %d has %d channels: each axis needs a positive even count <= d", a,
+                  axis_channels[a]);
     sum += axis_channels[a];
   }
   if (sum != d) return fail(DIT_ERR_INVALID, "axis channels sum to %d, not d=%d", sum, d);

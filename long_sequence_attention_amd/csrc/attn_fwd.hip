@@ -43,6 +43,11 @@
 //   * Pad query rows are computed but overwritten by a select in the epilogue.
 //   * XCD-aware workgroup order: consecutive q-tiles of a head run on one
 //     XCD so its K/V stay in that XCD's L2.
+//   * Segmented keys (ring layout): attn_fwd_seg_kernel runs the same key
+//     pipeline once per segment's real tiles, carrying the softmax state.
+//   * Fixed-m softmax (opt-in): a q-tile whose a-priori row bounds
+//     (fixed_m.hip) are tight enough runs the FIXED instance of the step,
+//     with the bound as its maximum: no running max and no rescale.
 #include "common.h"
 
 namespace dit {
