@@ -17,6 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libditattn.so")
+# the same sources with a wait and a barrier after every DMA issue and LDS
+# read phase of the attention kernel (results must equal LIB's bit for bit)
+LIB_DEBUG_SYNC = os.path.join(LIBDIR, "libditattn_debugsync.so")
 SOURCES = ["api.hip", "attn_fwd.hip", "elementwise.hip", "fixed_m.hip"]
 
 HIPCC_FLAGS = [
@@ -40,21 +43,37 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
+def _command(out, extra_flags):
+    return [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+
+
+def build(verbose: bool = False, extra_flags=None, debug_sync: bool = True) -> str:
+    """Compile LIB (and, unless debug_sync is False, LIB_DEBUG_SYNC alongside
+    it in a second compiler process); returns LIB's path."""
     os.makedirs(LIBDIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    jobs = [(LIB, list(extra_flags or []))]
+    if debug_sync:
+        jobs.append((LIB_DEBUG_SYNC, list(extra_flags or []) + ["-DDIT_DEBUG_SYNC=1"]))
+    procs = []
+    for out, flags in jobs:
+        cmd = _command(out + ".tmp", flags)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    failed = []
+    for out, proc in procs:
+        _, stderr = proc.communicate()
+        err = "\n".join(l for l in (stderr or "").splitlines() if noise not in l)
+        if proc.returncode != 0:
+            failed.append(f"{os.path.basename(out)}: hipcc failed ({proc.returncode}):\n{err}")
+            continue
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        os.replace(out + ".tmp", out)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     return LIB
 
 

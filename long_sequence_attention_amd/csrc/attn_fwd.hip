@@ -68,6 +68,22 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 __device__ __forceinline__ u32x4 ldg16(const bf16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Race check build (compiled with -DDIT_DEBUG_SYNC=1 into a separate
+// library): every wave waits for all of its outstanding global and LDS
+// accesses and meets the others at a barrier after each DMA issue and each
+// LDS read phase. The arithmetic is unchanged, so its results must equal
+// the pipelined build's bit for bit; a missing wait or barrier in the
+// pipeline would show up as a difference.
+#ifndef DIT_DEBUG_SYNC
+#define DIT_DEBUG_SYNC 0
+#endif
+__device__ __forceinline__ void debug_sync() {
+  if constexpr (DIT_DEBUG_SYNC != 0) {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
+    __syncthreads();
+  }
+}
+
 // Split-halves rotation of 8 channel pairs in fp32: x1 holds channels
 // i..i+7 of the first half, x2 the partners d/2 later.
 __device__ __forceinline__ void rotate8(float *x1, float *x2, const float *cv, const float *sv) {
@@ -227,6 +243,7 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
     issue_rows_par<D, G::K0>(par, cx.wbase, cx.kbase, cx.ks_bytes, t + 2, cx.kv_valid, cx.koff);
   if (HAS_NEXT)
     issue_rows_par<D, G::V0>(par ^ 1, cx.wbase, cx.vbase, cx.vs_bytes, t + 1, cx.kv_valid, cx.voff);
+  debug_sync();
   const char *vt = cx.smem + G::V0 + par * G::TILE_BYTES;
 
   const float neg_m = -m_run;
@@ -251,6 +268,7 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
     qk_tile<D>(cx.smem + G::K0 + (par ^ 1) * G::TILE_BYTES, kx, cx.qop, snext);
     if (!STEADY && mask_next) mask_tail(snext, (t + 1) * BN, cx.kv_valid, cx.hf);
   }
+  debug_sync();
   softmax_block(1);
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
@@ -266,6 +284,7 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
       }
     }
   }
+  debug_sync();
   float mts = 0.f;
   if (!FIXED && HAS_NEXT) mts = pair_max(snext) * cx.c2;
   if (STEADY) {
@@ -353,6 +372,7 @@ __device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &
   issue_rows<D, G::K0>(wbase, kbase, ln.ks_bytes, kb, kv_end, ln.koff);
   issue_rows<D, G::V0>(wbase, vbase, ln.vs_bytes, kb, kv_end, ln.voff);
   if (kb + 1 < ke) issue_rows<D, G::K0 + G::TILE_BYTES>(wbase, kbase, ln.ks_bytes, kb + 1, kv_end, ln.koff);
+  debug_sync();
 
   float m_fix = 0.f;
   if (FIRST) {

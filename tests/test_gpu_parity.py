@@ -786,6 +786,47 @@ def test_no_valid_keys_gives_zero_and_minus_inf(ops):
     assert (to_np_f64(o) == 0).all() and np.isneginf(to_np_f64(l)).all()
 
 
+@pytest.mark.parametrize("case", ["wan480", "wan480_fixed_m", "wan480_balanced", "ring_2_segments", "tiny_d64"])
+def test_race_check_build_is_bit_identical(ops, case):
+    """The race-check build of the library (a wait and a barrier after every
+    DMA issue and LDS read phase of the attention kernel, same arithmetic)
+    returns the same bits as the pipelined build: no result depends on a
+    missing wait or barrier."""
+    import ctypes
+    import torch
+    from long_sequence_attention_amd import _native as N
+    from long_sequence_attention_amd import build as Bd
+    say(f"race-check build: {case}")
+    Ld = ctypes.CDLL(Bd.LIB_DEBUG_SYNC)
+    Ld.dit_attn_fwd.argtypes = [ctypes.POINTER(N.AttnDesc), ctypes.c_void_p]
+    Ld.dit_attn_fwd.restype = ctypes.c_int
+    w = W.WORKLOADS["tiny" if case == "tiny_d64" else "wan480"]
+    q, k, v = W.make_qkv(w)
+    kw = dict(q_valid=w.s_valid, kv_valid=w.s_valid)
+    pos = W.positions(w)
+    if case == "ring_2_segments":
+        q, k, v, pos, per = _segmented_inputs(w, 2, 2368, 52)
+        kw = dict(q_valid=per, kv_valid=per, q_seg_len=2368, kv_seg_len=2368)
+    if case == "wan480_fixed_m":
+        kw["fixed_m"] = True
+    if case == "wan480_balanced":
+        kw["schedule"] = 2
+    tabs = ops.rope_split_tables(torch.from_numpy(pos).to(dev()), w.axes, w.d, w.theta)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    o1, l1 = ops.attn_fwd(qd, kd, vd, rope_q=tabs, rope_k=tabs, **kw)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    desc = ops._attn_desc(qd, kd, vd, o2, l2, kw["q_valid"], kw["kv_valid"], tabs, tabs, 0.0,
+                          kw.get("schedule", 0), q_seg_len=kw.get("q_seg_len", 0),
+                          kv_seg_len=kw.get("kv_seg_len", 0), fixed_m=kw.get("fixed_m", False))
+    need = ops.attn_workspace_size(qd, kd, vd, rope_q=tabs, rope_k=tabs, **kw)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev())
+    desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+    assert Ld.dit_attn_fwd(ctypes.byref(desc), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), case
+    assert torch.equal(l1, l2), case
+
+
 def test_binding_rejects_bad_caller_buffers(ops):
     """Caller-provided outputs of the wrong shape, dtype or layout, and
     operands on the wrong device, raise ValueError before any launch."""
