@@ -611,12 +611,13 @@ def test_bshd_strided_layout_equals_dense(ops):
 def test_wan720_single_pass_and_four_shard_merge(ops):
     import torch
     w = W.WORKLOADS["wan720"]
-    say("wan720 single pass + 4 key shards + merge (2048 sampled rows per head)")
+    say("wan720 single pass, fixed-m single pass, 4 key shards + merge (2048 sampled rows per head)")
     tabs = gpu_tables(ops, w)
     cos, sin = tabs
     q, k, v = W.make_qkv(w)
     qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
     o1, l1 = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs)
+    o3, l3 = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs, fixed_m=True)
     parts_o, parts_l = [], []
     for (s0, L, kvv) in W.key_shards(w):
         po, pl = ops.attn_fwd(qd, kd[:, :, s0:s0 + L], vd[:, :, s0:s0 + L], q_valid=w.s_valid, kv_valid=kvv,
@@ -632,11 +633,13 @@ def test_wan720_single_pass_and_four_shard_merge(ops):
         O_ref, L_ref = oracle.dit_path(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], pos, pos, w.axes, w.theta,
                                        w.s_valid, w.s_valid, rows=rows)
         valid = rows < w.s_valid
-        for tag, o, l in (("single", o1, l1), ("merged", o2, l2)):
+        for tag, o, l in (("single", o1, l1), ("fixed-m", o3, l3), ("merged", o2, l2)):
             og = to_np_f64(o[:, h:h + 1, rows])
             lg = to_np_f64(l[:, h:h + 1, rows])
             compare(og, lg, O_ref, L_ref, valid, f"wan720 h{h} {tag}")
             assert_pad_rows(og, lg, valid, f"wan720 h{h} {tag}")
+    # the fixed-m path ran (its rounding differs from the online path's somewhere)
+    assert not torch.equal(l1, l3)
 
 
 @pytest.mark.parametrize("cuts", [[0, 64, 128, 320], [0, 10, 10, 200, 320], [0, 300, 320], [0, 1, 320]])
