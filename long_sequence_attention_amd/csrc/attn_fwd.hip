@@ -40,7 +40,10 @@
 //     range. The result is unchanged in exact arithmetic.
 //   * Pad keys: tiles past kv_valid are never visited; in the tail tile,
 //     scores of keys >= kv_valid are replaced by -inf with a select.
-//   * Pad query rows are computed but overwritten by a select in the epilogue.
+//   * Pad query rows are computed but overwritten by a select in the
+//     epilogue; a wave whose 32 rows are all tail pads skips the arithmetic
+//     (it only issues its share of the K/V loads and meets the barriers),
+//     which lowers the power drawn by the last q-tile of each head.
 //   * XCD-aware workgroup order: consecutive q-tiles of a head run on one
 //     XCD so its K/V stay in that XCD's L2.
 //   * Segmented keys (ring layout): attn_fwd_seg_kernel runs the same key
@@ -373,6 +376,34 @@ __device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &
   issue_rows<D, G::V0>(wbase, vbase, ln.vs_bytes, kb, kv_end, ln.voff);
   if (kb + 1 < ke) issue_rows<D, G::K0 + G::TILE_BYTES>(wbase, kbase, ln.ks_bytes, kb + 1, kv_end, ln.koff);
   debug_sync();
+
+  // a wave whose 32 query rows are all tail pads (rows >= q_valid) does
+  // no arithmetic: it still issues its share of every K/V tile and meets
+  // the others at each barrier, and its rows are written as pads
+  if (p.q_seg_len == 0 && qt * BM + ln.wave * 32 >= p.q_valid) {
+    if (FIRST) {
+      l_run = 0.f;
+      m_run = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    __syncthreads();
+    for (int t = kb; t < ke; ++t) {
+      const int par = (t - kb) & 1;
+      if (t + 2 < ke) issue_rows_par<D, G::K0>(par, wbase, kbase, ln.ks_bytes, t + 2, kv_end, ln.koff);
+      if (t + 1 < ke) issue_rows_par<D, G::V0>(par ^ 1, wbase, vbase, ln.vs_bytes, t + 1, kv_end, ln.voff);
+      debug_sync();
+      debug_sync();
+      debug_sync();
+      if (t + 1 < ke) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
+    }
+    return;
+  }
 
   float m_fix = 0.f;
   if (FIRST) {
