@@ -174,11 +174,19 @@ __device__ __forceinline__ void issue_rows_par(int par, uint32_t wbase, const bf
   else issue_rows<D, BUF0>(wbase, base, row_bytes, t, kv_valid, off);
 }
 
+// S^T of one key tile: two 32-key blocks. hi = false (the tail tile when
+// its second block holds no real key): block 1 is not multiplied and its
+// scores are -inf, as the mask would make them.
 template <int D>
-__device__ __forceinline__ void qk_tile(const char *kt, int kx, const bf16x8 *qop, f32x16 *sacc) {
+__device__ __forceinline__ void qk_tile(const char *kt, int kx, const bf16x8 *qop, f32x16 *sacc, bool hi = true) {
   constexpr int DK = D / 16;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
+    if (blk == 1 && !hi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[1][r] = -INFINITY;
+      break;
+    }
     sacc[blk] = f32x16{};
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
@@ -266,15 +274,21 @@ __device__ __forceinline__ void step(const StepCtx<D> &cx, int t, int par, f32x1
       }
     }
   };
+  // tail tiles only: whether the second 32-key block of tile t (cur_hi) or
+  // of tile t+1 (next_hi) holds a real key; an empty block contributes
+  // p = 0 exactly, so its exp2, MFMAs and sums are skipped
+  const bool cur_hi = STEADY || t * BN + 32 < cx.kv_valid;
+  const bool next_hi = STEADY || !mask_next || (t + 1) * BN + 32 < cx.kv_valid;
   softmax_block(0);
   if (HAS_NEXT) {
-    qk_tile<D>(cx.smem + G::K0 + (par ^ 1) * G::TILE_BYTES, kx, cx.qop, snext);
+    qk_tile<D>(cx.smem + G::K0 + (par ^ 1) * G::TILE_BYTES, kx, cx.qop, snext, next_hi);
     if (!STEADY && mask_next) mask_tail(snext, (t + 1) * BN, cx.kv_valid, cx.hf);
   }
   debug_sync();
-  softmax_block(1);
+  if (cur_hi) softmax_block(1);
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
+    if (blk == 1 && !cur_hi) break;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
