@@ -387,7 +387,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the path shards by head across GPUs; see DESIGN.md)"}))
+                          "(across GPUs the path would shard by head: each GPU runs this kernel on its head share)"}))
         sys.exit(2)
     if args.traffic_summary:
         traffic_summary(args)
