@@ -386,7 +386,7 @@ def config_table(np, torch, ops, W, dev, n_iter):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 "
                           "(across GPUs the path would shard by head: each GPU runs this kernel on its head share)"}))
         sys.exit(2)
     if args.traffic_summary:
