@@ -161,7 +161,7 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   if (d->schedule < DIT_SCHED_AUTO || d->schedule > DIT_SCHED_BALANCED)
     return fail(DIT_ERR_INVALID, "schedule=%d is not a dit_schedule", d->schedule);
   // AUTO resolves to one workgroup per q-tile: on MI355X the key-split
-  // schedule measures slower on the Wan / FLUX / HunyuanVideo shapes (each
+  // schedule measures slower on the Wan, FLUX and HunyuanVideo shapes (each
   // piece pays a prologue, partial writes and a merge, its L2 reuse is
   // lower and the clock drops with every CU busy), so it runs only when
   // asked for.

@@ -9,8 +9,8 @@ What each function follows (pages are cited by title and section):
   * rope_tables / rope_split_halves / rope_interleaved /
     interleaved_to_split_permutation -- Difflet PR #153 "TPU sequence
     parallelism ...", the FLUX split-RoPE commit (channels permuted once to
-    [0, 2, ..., 1, 3, ...] so the pairwise rotation becomes a slice and a
-    concat; q.k is unchanged when both get the same permutation) and the Wan
+    [0, 2, ..., 1, 3, ...], which turns the pair rotation into slicing and
+    concatenation; q.k is unchanged when both get the same permutation) and the Wan
     padding + split RoPE commit (pad rows get the identity rotation). The
     per-axis frequency schedule is not printed on the pages; the plain
     reading used here is the standard 1-D schedule theta^(-2j/c_a) per axis
@@ -19,15 +19,16 @@ What each function follows (pages are cited by title and section):
     precedes RoPE (Difflet PR #153: the FLUX and Wan split-RoPE commits
     permute the q/k RMSNorm weights along with the channels).
   * attention -- softmax(scale * Q K^T) V over the valid keys only, with the
-    natural-log log-sum-exp per query row (mstar PR #376, "Ragged attention
-    returns the log-sum-exp": fp32, natural log). Pad keys are dropped
+    natural-log log-sum-exp per query row (mstar PR #376: the ragged
+    attention call can also hand back each row's log-sum-exp, fp32, natural
+    log). Pad keys are dropped
     exactly (Difflet PR #153, Wan padding commit; maxdiffusion PR #491, the
     ragged KV tail carries the real length). Pad query rows give O = 0 and
     LSE = -inf (a convention: -inf is the merge's identity).
   * segment_valid_rows / attention_segmented -- sequences cut into segments
-    that are each padded at their own tail (maxdiffusion PR #491: lane
-    padding per ring segment on the Ulysses-ring path; the padding
-    descriptor carries the real length and the segment count), attended as
+    that are each padded at their own tail (maxdiffusion PR #491: with ring
+    parallelism every segment gets its own tail padding, and the padding
+    descriptor holds the real length and the number of segments), attended as
     one softmax over every real key.
   * fixed_m_bound -- the a-priori row-max bound of the fixed-m softmax
     (maxdiffusion PR #491: fixed-m metadata from norm reductions and the key

@@ -167,8 +167,8 @@ def attention(q, k, v, q_valid: int, kv_valid: int, scale: float | None = None,
 def segment_valid_rows(S: int, seg_len: int, valid: int) -> np.ndarray:
     """Indices of the real rows of a sequence of S rows cut into segments of
     seg_len rows, each holding `valid` real rows followed by its own tail
-    pad (maxdiffusion PR #491: on the Ulysses-ring path each ring segment is
-    padded at its own tail)."""
+    pad (maxdiffusion PR #491: with ring parallelism every segment carries
+    its own tail padding)."""
     if seg_len <= 0 or S % seg_len:
         raise ValueError("S must be a positive multiple of seg_len")
     r = np.arange(S)

@@ -154,8 +154,8 @@ def _raw_qk_with_row_scales(w, seed):
 ])
 def test_fused_qk_rmsnorm_rope(ops, case):
     """Per-head q/k RMSNorm with weights fused into the pre-pass before RoPE
-    (Difflet PR #153 split-RoPE commits: the q/k RMSNorm weights are permuted
-    with the channels), against the oracle's fp64 norm -> RoPE -> attention,
+    (Difflet PR #153 split-RoPE commits: the RMSNorm weights of q and k
+    follow the channel permutation), against the oracle's fp64 norm -> RoPE -> attention,
     graded at the same bar; pad query rows stay 0 / -inf."""
     import torch
     w = W.WORKLOADS[case["name"]]
