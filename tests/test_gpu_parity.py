@@ -398,7 +398,7 @@ def _random_case(seed):
     return c
 
 
-@pytest.mark.parametrize("seed", list(range(60, 72)))
+@pytest.mark.parametrize("seed", list(range(60, 84)))
 def test_random_shapes_against_oracle(ops, seed):
     """Seeded random shapes and options (ragged lengths including 0, d 64 /
     128, dense or token-major strides, RoPE on Q and / or K, fused norm,
@@ -468,14 +468,15 @@ def _random_segment_case(seed):
              n_kseg=int(r.integers(1, 4)), kv_seg_len=kl, kv_valid=int(r.integers(1, kl + 1)),
              n_qseg=int(r.integers(1, 4)), q_seg_len=ql, q_valid=int(r.integers(0, ql + 1)),
              rope_q=bool(r.random() < 0.6), rope_k=bool(r.random() < 0.6), fixed_m=bool(r.random() < 0.4))
+    c["norm"] = bool(r.random() < 0.3)
     return c
 
 
-@pytest.mark.parametrize("seed", list(range(80, 88)))
+@pytest.mark.parametrize("seed", list(range(80, 96)))
 def test_random_segmented_against_oracle(ops, seed):
     """Seeded random ring layouts: 1-3 key segments and 1-3 query segments of
     64-multiple lengths, each padded at its own tail with garbage, d 64 /
-    128, RoPE on Q and / or K, online or fixed-m softmax; against the
+    128, RoPE on Q and / or K, fused q/k norm, online or fixed-m softmax; against the
     oracle's segmented attention on the bf16-rounded prepared Q/K (O within
     the derived bound, LSE within the derived bound of the unrounded
     oracle); pad rows 0 / -inf."""
@@ -499,11 +500,17 @@ def test_random_segmented_against_oracle(ops, seed):
     pk[krows, 0] = r.integers(0, 200, len(krows))
     tq = ops.rope_split_tables(torch.from_numpy(pq).to(dev()), (d,), d, 10000.0) if c["rope_q"] else None
     tk = ops.rope_split_tables(torch.from_numpy(pk).to(dev()), (d,), d, 10000.0) if c["rope_k"] else None
+    wq = (1.0 + 0.2 * r.standard_normal(d)).astype(np.float32)
+    wk = (1.0 + 0.2 * r.standard_normal(d)).astype(np.float32)
     o, l = ops.attn_fwd(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), q_valid=c["q_valid"],
                         kv_valid=c["kv_valid"], q_seg_len=c["q_seg_len"], kv_seg_len=c["kv_seg_len"],
-                        rope_q=tq, rope_k=tk, fixed_m=c["fixed_m"])
+                        rope_q=tq, rope_k=tk, fixed_m=c["fixed_m"],
+                        q_norm=torch.from_numpy(wq).to(dev()) if c["norm"] else None,
+                        k_norm=torch.from_numpy(wk).to(dev()) if c["norm"] else None)
     torch.cuda.synchronize()
     qf, kf, vf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(k), oracle.bf16_to_f64(v)
+    if c["norm"]:
+        qf, kf = oracle.rms_norm(qf, wq, 1e-6), oracle.rms_norm(kf, wk, 1e-6)
     if c["rope_q"]:
         qf = oracle.rope_split_halves(qf, *oracle.rope_tables(pq, (d,), 10000.0))
     if c["rope_k"]:
