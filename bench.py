@@ -179,11 +179,10 @@ def pmc_target(args):
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     _, (qd, kd, vd) = dev_tensors(w, np, torch, dev)
-    cos, sin = ops.rope_split_tables(torch.from_numpy(W.positions(w)).to(dev), w.axes, w.d, w.theta)
     o = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev)
     for _ in range(5):
-        ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=None, rope_k=None, out=o, lse=lse)
+        ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=None, rope_k=None, out=o, lse=lse)
     src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
     src.fill_(1)
     dst = torch.empty_like(src)
