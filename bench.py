@@ -80,24 +80,27 @@ def sclk_levels():
     return out or None
 
 
-def device_info(torch, sclk_busy):
+def device_info(torch, sclk_busy, sclk_kernel=None):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
-            "sclk_during_timed_steps": sclk_busy, "sclk_after": sclk_levels(),
+            "sclk_during_timed_steps": sclk_busy, "sclk_during_kernel_loop": sclk_kernel,
+            "sclk_after": sclk_levels(),
             "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
 
 
-def dev_tensors(w, np, torch, dev):
+def dev_tensors(w, np, torch, dev, inputs=None):
     import workloads as W
-    q, k, v = W.make_qkv(w)
+    q, k, v = inputs[w.name] if inputs and w.name in inputs else W.make_qkv(w)
     tod = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
     return (q, k, v), (tod(q), tod(k), tod(v))
 
 
-def time_us(torch, fn, n, warm=3, warm_s=0.0):
+def time_us(torch, fn, n, warm=3, warm_s=0.0, clock=None):
     """Average microseconds per call of fn over n back-to-back calls, HIP
     events on torch's current stream (the stream every dit_* call uses),
-    after `warm` calls and at least warm_s seconds of calls."""
+    after `warm` calls and at least warm_s seconds of calls. With a list
+    `clock`, the sysfs shader-clock levels read while the timed calls are
+    still queued are appended to it."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
@@ -111,33 +114,151 @@ def time_us(torch, fn, n, warm=3, warm_s=0.0):
     for _ in range(n):
         fn()
     b.record()
+    if clock is not None:
+        clock.append(sclk_levels())
     torch.cuda.synchronize()
     return a.elapsed_time(b) / n * 1e3
 
 
-def cpu_baseline(w, q, k, v, budget_s=10.0):
-    """The fp64 oracle as it stands, timed on this host over the whole
-    workload (all heads, all valid rows): repeated runs for about budget_s
-    seconds of CPU work (at least three), the median run reported."""
+CONFIGS = ("tiny", "flux", "wan480", "hunyuan", "wan720")
+SETTLE_S = 1.0              # minimum seconds of warm-up steps before the timed ones
+ORACLE_ROW_BLOCK = 1024     # query rows per oracle task
+MAX_POOL = 16               # the host share of one GPU on the box
+
+
+def pool_size():
+    return max(1, min(len(os.sched_getaffinity(0)), MAX_POOL))
+
+
+BLAS_ENV = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+
+
+def _worker_init():
+    """Each worker runs the oracle on one BLAS thread (the pool spreads the
+    work over the cores); the environment set by spawn_pool covers the BLAS
+    library loaded later, the limit here one already loaded."""
+    import numpy  # noqa: F401  (loads BLAS, so the limit below applies to it)
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def spawn_pool(n):
+    """A pool of n spawned worker processes, each limited to one BLAS thread."""
+    import multiprocessing as mp
+    saved = {k: os.environ.get(k) for k in BLAS_ENV}
+    os.environ.update({k: "1" for k in BLAS_ENV})
+    try:
+        return mp.get_context("spawn").Pool(n, initializer=_worker_init)
+    finally:
+        for k, val in saved.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+
+
+def _gen_head(task):
+    """Seeded synthetic inputs of one head (all batches): bf16 bits [B, S, d] x 3."""
+    import numpy as np
+    import workloads as W
+    name, h = task
+    w = W.WORKLOADS[name]
+    return name, h, [np.stack([W.make_head(w, t, b, h) for b in range(w.B)]) for t in "qkv"]
+
+
+def make_inputs(names, pool):
+    """Q, K, V bf16 bit arrays [B, H, S, d] of every named workload, generated
+    head by head in the pool (the same bits as workloads.make_qkv)."""
+    import numpy as np
+    import workloads as W
+    out = {}
+    for name in names:
+        w = W.WORKLOADS[name]
+        out[name] = [np.empty((w.B, w.H, w.s_pad if t == "q" else w.k_pad, w.d), dtype=np.uint16) for t in "qkv"]
+    for name, h, arrs in pool.imap_unordered(_gen_head, [(n, h) for n in names for h in range(W.WORKLOADS[n].H)]):
+        for dst, a in zip(out[name], arrs):
+            dst[:, h] = a
+    return {n: tuple(v) for n, v in out.items()}
+
+
+def _oracle_task(task):
+    """The fp64 oracle (RoPE tables, RoPE, masked attention, LSE) on the
+    given query rows of one head; returns its wall time and, when asked,
+    the result."""
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    name, h, rows, q, k, v, keep = task
+    w = W.WORKLOADS[name]
     pos = W.positions(w)
-    walls = []
-    t_start = time.perf_counter()
-    while len(walls) < 3 or (time.perf_counter() - t_start < budget_s and len(walls) < 50):
+    t0 = time.perf_counter()
+    O, L = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid, rows=rows)
+    dt = time.perf_counter() - t0
+    return name, h, rows, dt, (O, L) if keep else None
+
+
+def oracle_rows(w):
+    """Query rows the oracle times per head: every valid row, or 2048 seeded
+    sampled rows per head for the 720p shard."""
+    import numpy as np
+    import workloads as W
+    if w.n_key_shards > 1:
+        return [W.sample_rows(w, h) for h in range(w.H)], "2048 seeded sampled valid query rows per head"
+    return [np.arange(w.s_valid)] * w.H, "all valid query rows"
+
+
+def cpu_baseline_all(inputs, pool, keep=("wan480",)):
+    """The fp64 oracle as it stands, timed on this host's cores for every
+    config: one task per (head, block of up to 1024 query rows), spread over
+    a process pool of one single-threaded worker per core; wall time per
+    config measured around the whole pool map (inputs shipped to the workers
+    included). Returns the per-config figures and the full results of the
+    configs in `keep`."""
+    import numpy as np
+    import workloads as W
+    per, results = {}, {}
+    for name in CONFIGS:
+        w = W.WORKLOADS[name]
+        q, k, v = inputs[name]
+        rows_per_head, what = oracle_rows(w)
+        tasks = []
+        for h in range(w.H):
+            rh = rows_per_head[h]
+            for r0 in range(0, len(rh), ORACLE_ROW_BLOCK):
+                tasks.append((name, h, rh[r0:r0 + ORACLE_ROW_BLOCK], q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1],
+                              name in keep))
+        n_rows = sum(len(r) for r in rows_per_head)
+        flop = 4.0 * w.B * n_rows * w.k_valid * w.d
         t0 = time.perf_counter()
-        ref = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
-        walls.append(time.perf_counter() - t0)
-    dt = sorted(walls)[len(walls) // 2]
-    return {"value": w.valid_flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full {w.name} workload (B={w.B}, H={w.H}, all {w.s_valid} valid query rows, RoPE tables, "
-                      f"RoPE, attention, LSE), NumPy float64, median of {len(walls)} runs "
-                      f"({sum(walls):.1f} s in all): {dt:.2f} s wall per run"}, ref
+        outs = list(pool.imap_unordered(_oracle_task, tasks))
+        wall = time.perf_counter() - t0
+        ent = {"wall_s": wall, "task_s_sum": sum(o[3] for o in outs), "tasks": len(tasks), "rows": what,
+               "query_rows_computed": n_rows, "flop_computed": flop, "gflops": flop / wall / 1e9}
+        if n_rows < w.H * w.B * w.s_valid:
+            ent["full_workload_s_extrapolated"] = wall * w.valid_flop / flop
+            ent["note"] = "full_workload_s_extrapolated scales the sampled wall time to all valid rows (not measured)"
+        per[name] = ent
+        if name in keep:
+            O = np.zeros((w.B, w.H, w.s_pad, w.d))
+            L = np.full((w.B, w.H, w.s_pad), -np.inf)
+            for _, h, rows, _, (Ob, Lb) in outs:
+                O[:, h, rows] = Ob[:, 0]
+                L[:, h, rows] = Lb[:, 0]
+            results[name] = (O, L)
+    return per, results
+
+
+def cpu_baseline_line(per, workers):
+    w3 = per["wan480"]
+    return {"value": w3["gflops"] / 1e3, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": (f"full wan480 workload (B=1, H=10, all 4680 valid query rows: RoPE tables, RoPE, masked "
+                       f"attention, LSE), NumPy float64, {w3['tasks']} tasks of <= {ORACLE_ROW_BLOCK} query rows "
+                       f"over {workers} single-threaded worker processes: {w3['wall_s']:.2f} s wall; every config "
+                       f"in per_config (720p on 2048 sampled rows per head)"),
+            "affinity_cores": len(os.sched_getaffinity(0)), "workers": workers, "blas_threads_per_worker": 1,
+            "per_config": per}
 
 
 def parity_of_step(np, o_tok, lse, ref, s_valid):
@@ -285,7 +406,7 @@ def traffic_summary(args):
 
 
 # -------------------------------------------------------------- the bench
-def config_table(np, torch, ops, W, dev, n_iter):
+def config_table(np, torch, ops, W, dev, n_iter, inputs=None):
     """Attention throughput on every config (dit_attn_fwd call = Q / K
     rotation pre-pass + attention kernel, or the kernel alone for the
     cross-attention config, which has no RoPE; the Wan 720p config also as 4 key shards plus
@@ -293,7 +414,7 @@ def config_table(np, torch, ops, W, dev, n_iter):
     res = {}
     for name in ("tiny", "flux", "wan480", "hunyuan", "wan720", "xattn480"):
         w = W.WORKLOADS[name]
-        _, (qd, kd, vd) = dev_tensors(w, np, torch, dev)
+        _, (qd, kd, vd) = dev_tensors(w, np, torch, dev, inputs)
         cos, sin = ops.rope_split_tables(torch.from_numpy(W.positions(w)).to(dev), w.axes, w.d, w.theta)
         tabs = (cos, sin) if w.rope else None
         o = torch.empty_like(qd)
@@ -399,16 +520,32 @@ def main():
         return
     import ctypes
     import numpy as np
-    import torch
     import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    # Host work first, before anything touches the GPU: the seeded inputs of
+    # every config (and, unless skipped, the oracle timed on them) in a pool
+    # of spawned single-threaded workers, one per core.
+    names = [args.workload]
+    if not args.no_configs:
+        names += [n for n in CONFIGS + ("xattn480",) if n not in names]
+    cpu_per, refs, workers = None, {}, pool_size()
+    if args.no_cpu_baseline:
+        inputs = {n: W.make_qkv(W.WORKLOADS[n]) for n in names}
+    else:
+        names += [n for n in CONFIGS if n not in names]
+        with spawn_pool(workers) as pool:
+            inputs = make_inputs(names, pool)
+            cpu_per, refs = cpu_baseline_all(inputs, pool, keep=(args.workload,))
+
+    import torch
     import long_sequence_attention_amd as ops
 
     ops.library_path()  # fails loudly if the HIP library is not built
-    w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     B, H, d, Sv, Sp = w.B, w.H, w.d, w.s_valid, w.s_pad
 
-    (q, k, v), _ = dev_tensors(w, np, torch, torch.device("cpu"))
+    q, k, v = inputs[args.workload]
 
     # token-major fused QKV [B, S_valid, 3, H, d]: what one all-to-all of the
     # stacked Q, K, V hands over (sequence shard -> head shard)
@@ -444,6 +581,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # whatever --warmup says, at least SETTLE_S seconds of steps: the shader
+    # clock settles only after some hundreds of ms of sustained load
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -465,7 +609,8 @@ def main():
                      out=op.transpose(1, 2), lse=lse)
 
     n = args.kernel_iters
-    us_attn = time_us(torch, attn_only, n, warm_s=1.0)
+    sclk_kernel = []
+    us_attn = time_us(torch, attn_only, n, warm_s=1.0, clock=sclk_kernel)
     us_tables = time_us(torch, lambda: ops._native.check(L.dit_rope_split_tables(
         ctypes.c_void_p(pos.data_ptr()), Sp, len(w.axes), chans, d, float(w.theta), ctypes.c_void_p(cos.data_ptr()),
         ctypes.c_void_p(sin.data_ptr()), ops._stream(dev)), "tables"), n)
@@ -509,14 +654,19 @@ def main():
                        "pad_qkv_GBps": 3 * pad_bytes / (us_pad_qkv * 1e-6) / 1e9,
                        "unpad_GBps": 2 * Sv * H * d * 2 * B / (us_unpad * 1e-6) / 1e9},
         "pct_of_peak_step": flop / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS * 100,
-        "device": device_info(torch, sclk_busy),
+        # the dit_attn_fwd call (Q/K RoPE pre-pass + attention kernel) and the
+        # attention kernel alone, against the bf16 dense peak
+        "call_tflops": flop / (us_call * 1e-6) / 1e12,
+        "call_pct_of_peak": flop / (us_call * 1e-6) / 1e12 / PEAK_BF16_TFLOPS * 100,
+        "kernel_pct_of_peak": achieved / PEAK_BF16_TFLOPS * 100,
+        "device": device_info(torch, sclk_busy, sclk_kernel[0] if sclk_kernel else None),
     }
     del k_rot
     if not args.no_configs:
-        out["configs_attn_fwd"] = config_table(np, torch, ops, W, dev, n)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"], ref = cpu_baseline(w, q, k, v)
-        out["step_parity_vs_oracle"] = parity_of_step(np, o_tok, lse, ref, Sv)
+        out["configs_attn_fwd"] = config_table(np, torch, ops, W, dev, n, inputs)
+    if cpu_per is not None:
+        out["cpu_baseline"] = cpu_baseline_line(cpu_per, workers)
+        out["step_parity_vs_oracle"] = parity_of_step(np, o_tok, lse, refs[args.workload], Sv)
     print(json.dumps(out), flush=True)
 
 

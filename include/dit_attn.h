@@ -219,7 +219,13 @@ DIT_API int dit_pad_tokens(const void *in, void *out, int B, int s_valid, int s_
 DIT_API int dit_unpad_tokens(const void *in, void *out, int B, int s_pad, int s_valid,
                      int64_t row_bytes, void *stream);
 
-/* Host helper: *s_pad_out = ceil(s_valid / multiple) * multiple. */
+/* Host helper: *s_pad_out = ceil(s_valid / multiple) * multiple, the tail
+ * padding plan of the pages: Difflet PR #153, Wan padding + split RoPE commit
+ * (4680 tokens padded to 4736, a multiple of 128; the LTX-2 scope pads to a
+ * multiple of 2*tp, 2310 -> 2312) and maxdiffusion PR #491, lane padding
+ * (each shard a multiple of 128 rows, 75,600 -> 75,776 at CP=4).
+ * DIT_ERR_INVALID: s_pad_out NULL, multiple <= 0, s_valid < 0, or a padded
+ * length beyond INT32_MAX. No HIP call is made. */
 DIT_API int dit_plan_padding(int s_valid, int multiple, int *s_pad_out);
 
 /* Thread-local description of the last non-OK status ("" if none). */

@@ -36,6 +36,34 @@ HIPCC_FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """sha256 (16 hex digits) of every library source and header: written
+    next to the library at build time, so a library older than its sources
+    can be told apart."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h", ".hpp", ".cpp")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+HASH_FILE = LIB + ".srchash"
+
+
+def is_current() -> bool:
+    """Both libraries exist and were built from the sources as they are now."""
+    try:
+        with open(HASH_FILE) as f:
+            recorded = f.read().strip()
+    except OSError:
+        return False
+    return os.path.exists(LIB) and os.path.exists(LIB_DEBUG_SYNC) and recorded == source_hash()
+
+
 def hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -74,6 +102,9 @@ def build(verbose: bool = False, extra_flags=None, debug_sync: bool = True) -> s
         os.replace(out + ".tmp", out)
     if failed:
         raise RuntimeError("\n".join(failed))
+    if debug_sync and not extra_flags:
+        with open(HASH_FILE, "w") as f:
+            f.write(source_hash() + "\n")
     return LIB
 
 

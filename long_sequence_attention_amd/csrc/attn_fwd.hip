@@ -134,14 +134,17 @@ struct Geo {
 // for: the kernel orders these loads itself (s_waitcnt vmcnt(0) and a
 // barrier before a filled buffer is read). M0 = wbase + OFF is formed inside
 // the statement (one wait state before the load reads it), so the 16
-// distinct LDS targets of a step do not each hold an SGPR. No other code in
-// these kernels uses M0.
+// distinct LDS targets of a step do not each hold an SGPR. M0 is a declared
+// output of the statement ("={m0}"), so the compiler knows the statement
+// overwrites it and keeps no value of its own there across it.
 template <int OFF>
 __device__ __forceinline__ void lds_dma16(uint32_t wbase, int voff, i32x4 rsrc) {
-  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
+  uint32_t m0_out;
+  asm volatile("s_add_u32 m0, %1, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               : "={m0}"(m0_out)
                : "s"(wbase), "v"(voff), "s"(rsrc), "i"(OFF)
                : "memory", "scc");
+  (void)m0_out;
 }
 
 // Issue this wave's share of tile t of K or V into LDS buffer BUF (byte

@@ -12,9 +12,13 @@ TOL_LSE = 5e-3         # LSE abs
 
 
 def ensure_built():
+    """Load the library, building it first when it is missing or was built
+    from other sources than the ones in the tree (hash recorded at build
+    time), so a stale library is never tested against newer sources."""
     from long_sequence_attention_amd import _native as N
-    if not os.path.exists(N.LIB_PATH):
-        from long_sequence_attention_amd import build
+    from long_sequence_attention_amd import build
+    if not build.is_current():
+        print("library missing or older than its sources: building it", flush=True)
         build.build()
     return N.lib()
 

@@ -658,6 +658,60 @@ def test_wan720_single_pass_and_four_shard_merge(ops):
     assert not torch.equal(l1, l3)
 
 
+def test_wan720_pad_refill_bit_exact(ops):
+    """Wan 720p (75600 real rows padded to 75648): refilling the 48 pad rows
+    of Q, K and V with a second finite-garbage draw, and with NaN, +Inf, -Inf
+    and an all-ones pattern, changes no bit of O or LSE on any row, for the
+    single pass and for the 4 key shards (the last shard holds the pads)
+    plus dit_lse_merge, including the last shard's fp32 partial."""
+    import torch
+    w = W.WORKLOADS["wan720"]
+    say("wan720 pad refill: single pass and 4 key shards + merge")
+    cos, sin = gpu_tables(ops, w)
+    q, k, v = W.make_qkv(w)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    del q, k, v
+    shards = W.key_shards(w)
+    assert shards[-1][2] < shards[-1][1]   # the last shard ends in the pad rows
+    o1 = torch.empty((w.B, w.H, w.s_pad, w.d), dtype=torch.bfloat16, device=dev())
+    l1 = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev())
+    om, lm = torch.empty_like(o1), torch.empty_like(l1)
+    po = [torch.empty((w.B, w.H, w.s_pad, w.d), dtype=torch.float32, device=dev()) for _ in shards]
+    pl = [torch.empty_like(l1) for _ in shards]
+
+    def run():
+        ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=(cos, sin), rope_k=(cos, sin),
+                     out=o1, lse=l1)
+        for i, (s0, L, kvv) in enumerate(shards):
+            ops.attn_fwd(qd, kd[:, :, s0:s0 + L], vd[:, :, s0:s0 + L], q_valid=w.s_valid, kv_valid=kvv,
+                         rope_q=(cos, sin), rope_k=(cos[s0:s0 + L], sin[s0:s0 + L]), out=po[i], lse=pl[i])
+        ops.lse_merge(po, pl, q_valid=w.s_valid, out=om, lse_out=lm)
+        torch.cuda.synchronize()
+        return [x.clone() for x in (o1, l1, om, lm, po[-1], pl[-1])]
+
+    names = ("single O", "single LSE", "merged O", "merged LSE", "last shard O", "last shard LSE")
+    ref = run()
+    tail = slice(w.s_valid - 8, w.s_pad)   # the last 8 real rows and the 48 pad rows
+    assert_pad_rows(to_np_f64(ref[0][:, :, tail]), to_np_f64(ref[1][:, :, tail]),
+                    np.arange(w.s_pad)[tail] < w.s_valid, "wan720 single")
+    n_pad = w.s_pad - w.s_valid
+    r = np.random.default_rng(72)
+    fills = [("second garbage draw", None)] + [(hex(p), p) for p in (0x7FC0, 0x7F80, 0xFF80, 0xFFFF)]
+    for tag, pattern in fills:
+        for x in (qd, kd, vd):
+            if pattern is None:
+                x[:, :, w.s_valid:] = to_dev_bf16(W.finite_garbage_bits(r, (w.B, w.H, n_pad, w.d)))
+            else:
+                x[:, :, w.s_valid:] = torch.from_numpy(np.array([pattern], dtype=np.uint16).view(np.int16)).to(
+                    dev()).view(torch.bfloat16)
+        got = run()
+        for name, a, b in zip(names, ref, got):
+            ia = a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
+            ib = b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)
+            assert torch.equal(ia, ib), (tag, name)
+        say(f"wan720 pad refill {tag}: every bit unchanged")
+
+
 @pytest.mark.parametrize("cuts", [[0, 64, 128, 320], [0, 10, 10, 200, 320], [0, 300, 320], [0, 1, 320]])
 def test_uneven_shards_and_empty_shard_merge(ops, cuts):
     import torch
@@ -779,8 +833,10 @@ def test_sharp_softmax_q_times_8(ops):
     # rotations, where a rescale error would still show as an O(|O|) miss
     O_rr, L_rr = _edge.rounded_ref
     otol = o_rounding_bound(O_rr, _edge.v)
-    res = compare(og, lg, O_rr, L_rr, valid, "sharp vs rounded-rotation oracle", o_tol=otol)
-    assert res["o_max_rel_to_rms"] < 0.03
+    # every element within u (|O| + max|v|) + 1e-4 (bf16 rounding of P and O):
+    # that bound is the whole O check; the relative-to-RMS figure is printed
+    # for information only
+    compare(og, lg, O_rr, L_rr, valid, "sharp vs rounded-rotation oracle", o_tol=otol)
     # and against the unrounded oracle within the derived LSE bound
     dl = np.abs(lg[:, :, valid] - L_ref[:, :, valid])
     assert (dl <= bound[:, :, valid]).all()

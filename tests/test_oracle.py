@@ -458,6 +458,77 @@ def test_dit_path_tiny_rows_and_properties():
     assert abs(np.mean(L[:, :, :300]) - (math.log(300) + 0.5)) < 0.3
 
 
+def _distinct_positions(seed, S_q, S_kv, n_axes):
+    r = rng(seed)
+    return (r.integers(0, 50, (S_q, n_axes)).astype(np.int64), r.integers(0, 50, (S_kv, n_axes)).astype(np.int64))
+
+
+def _bits(seed, shape):
+    return W.bf16_bits(rng(seed).standard_normal(shape).astype(np.float32))
+
+
+def test_dit_path_common_position_shift_changes_nothing():
+    """Query and key positions differ (pos_q != pos_k); shifting BOTH sets by
+    the same per-axis offset leaves every score, so O and LSE, unchanged:
+    RoPE scores depend on position differences only (the relative-position
+    reason the pages give for the rotation)."""
+    axes, d = (8, 12, 12), 32
+    q, k, v = _bits(60, (1, 2, 9, d)), _bits(61, (1, 2, 13, d)), _bits(62, (1, 2, 13, d))
+    pq, pk = _distinct_positions(63, 9, 13, 3)
+    O1, L1 = oracle.dit_path(q, k, v, pq, pk, axes, 100.0, 9, 11)
+    delta = np.array([[17, -5, 300]])
+    O2, L2 = oracle.dit_path(q, k, v, pq + delta, pk + delta, axes, 100.0, 9, 11)
+    assert np.allclose(O1, O2, rtol=0, atol=1e-12) and np.allclose(L1, L2, rtol=0, atol=1e-12)
+    # shifting only the keys does change the result (the pin is not vacuous)
+    O3, _ = oracle.dit_path(q, k, v, pq, pk + delta, axes, 100.0, 9, 11)
+    assert not np.allclose(O1, O3, atol=1e-6)
+
+
+def test_dit_path_zero_key_positions_rotate_the_queries_only():
+    """Key positions all 0 (the identity rotation) with pos_q != 0: the path
+    equals attention of the rotated queries over the unrotated keys."""
+    axes, d = (64,), 64
+    q, k, v = _bits(64, (1, 1, 7, d)), _bits(65, (1, 1, 10, d)), _bits(66, (1, 1, 10, d))
+    pq, _ = _distinct_positions(67, 7, 10, 1)
+    pk0 = np.zeros((10, 1), dtype=np.int64)
+    O, L = oracle.dit_path(q, k, v, pq, pk0, axes, 10000.0, 7, 10)
+    c, s = oracle.rope_tables(pq, axes, 10000.0)
+    O2, L2 = oracle.attention(oracle.rope_split_halves(oracle.bf16_to_f64(q), c, s), oracle.bf16_to_f64(k),
+                              oracle.bf16_to_f64(v), 7, 10)
+    assert np.allclose(O, O2, rtol=0, atol=1e-13) and np.allclose(L, L2, rtol=0, atol=1e-13)
+
+
+def test_dit_path_scores_match_complex_relative_angles():
+    """Independent route to the whole path with distinct positions: with
+    z = x_i + i x_{i+d/2} per channel pair, the split-halves rotation
+    multiplies z by e^{i w p}, so the score is
+        scale * Re(sum_i z_q,i conj(z_k,i) e^{i w_i (p_q - p_k)}),
+    evaluated here in numpy complex arithmetic; LSE from scipy's logsumexp
+    and O from the softmax weights. Swapping the query and key tables flips
+    the relative angle and fails this pin."""
+    axes, d, theta = (16, 8, 8), 32, 500.0
+    Sq, Skv, kv_valid = 6, 11, 9
+    q, k, v = _bits(68, (1, 1, Sq, d)), _bits(69, (1, 1, Skv, d)), _bits(70, (1, 1, Skv, d))
+    pq, pk = _distinct_positions(71, Sq, Skv, 3)
+    O, L = oracle.dit_path(q, k, v, pq, pk, axes, theta, Sq, kv_valid)
+    qf, kf, vf = (oracle.bf16_to_f64(x)[0, 0] for x in (q, k, v))
+    h = d // 2
+    zq = qf[:, :h] + 1j * qf[:, h:]
+    zk = kf[:kv_valid, :h] + 1j * kf[:kv_valid, h:]
+    # per-pair frequencies written out: axis a with c_a channels, pair j turns at theta^(-2j/c_a)
+    w = np.concatenate([theta ** (-2.0 * np.arange(c // 2) / c) for c in axes])
+    ax = np.concatenate([np.full(c // 2, a) for a, c in enumerate(axes)])
+    dp = pq[:, None, ax] - pk[None, :kv_valid, ax]                       # [Sq, kv, h]
+    s = np.real((zq[:, None, :] * np.conj(zk)[None, :, :] * np.exp(1j * w * dp)).sum(-1)) / math.sqrt(d)
+    L_ref = scipy.special.logsumexp(s, axis=1)
+    O_ref = np.exp(s - L_ref[:, None]) @ vf[:kv_valid]
+    assert np.allclose(L[0, 0], L_ref, rtol=0, atol=1e-12)
+    assert np.allclose(O[0, 0], O_ref, rtol=0, atol=1e-12)
+    # negative control: the tables swapped between Q and K (relative angle negated)
+    s_sw = np.real((zq[:, None, :] * np.conj(zk)[None, :, :] * np.exp(-1j * w * dp)).sum(-1)) / math.sqrt(d)
+    assert not np.allclose(L_ref, scipy.special.logsumexp(s_sw, axis=1), atol=1e-6)
+
+
 # ------------------------------------------------------------------ negative controls
 def test_negative_control_missing_mask_breaks_pad_invariance():
     q, k, v = rand_qkv(21, 1, 1, 16, 32, 64)
