@@ -58,13 +58,21 @@ typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
 /* How dit_attn_fwd spreads work over the GPU (results agree to rounding;
  * each schedule is bit-reproducible from call to call):
  * PER_QTILE runs one workgroup per 256-row query tile over all keys.
- * BALANCED splits the key range of every query tile into 2..8 equal pieces
- * (the count chosen from the device's compute-unit count to even out the
- * last wave of workgroups); each piece writes fp32 partial results to the
- * workspace and the last piece of a tile to finish merges them in a fixed
- * order (no workgroup waits for another).
- * AUTO resolves to PER_QTILE, which measures faster on MI355X for the
- * Wan, FLUX and HunyuanVideo shapes. */
+ * BALANCED (Stream-K) runs one workgroup per compute unit: the launch's
+ * (query tile, 64-key tile) units, query-tile major, are cut into equal
+ * contiguous ranges, one per workgroup, so every compute unit gets the same
+ * work; a query tile whose keys span two or three ranges is finished in
+ * pieces: each piece writes fp32 partial results to the workspace and the
+ * last piece of the tile to arrive merges them in key order (no workgroup
+ * waits for another). It covers one-segment, online-softmax calls with at
+ * least two key tiles; other calls run PER_QTILE.
+ * With fewer query tiles than compute units, BALANCED keeps one "main"
+ * workgroup per query tile on the keys' head (all in step, so each K/V tile
+ * is read while it is in L2) and lets the spare compute units split the
+ * remaining key tails. AUTO resolves to PER_QTILE: on MI355X the split
+ * measured slower on every shape tried (the chip is power-limited, so the
+ * clock falls as the spare compute units join, and the partial results'
+ * store and merge cost more than the shorter key range saves). */
 typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED = 2 } dit_schedule;
 
 /*
@@ -100,12 +108,21 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  *
  * workspace: device scratch for the once-per-call rotated (and normalised)
  * copies of K and Q (dense bf16 [B, H, s, d] each, when their tables or norm
- * weights are given), under the BALANCED schedule the partial results of
- * split query tiles and their arrival counters, and with fixed_m the key
- * and query statistics (fp32, about B*H*(s_q + 2*d + s_kv*d/256) values). Required (non-NULL, 256-byte aligned, at least
+ * weights are given), under the BALANCED schedule (also when AUTO picks it)
+ * two fp32 partial-result slots per workgroup (2 * CUs * (256 KB / 128 * d
+ * + 1 KB)) and one int32 arrival counter per query tile, and with fixed_m
+ * the key and query statistics (fp32, about B*H*(s_q + 2*d + s_kv*d/256)
+ * values). Required (non-NULL, 256-byte aligned, at least
  * dit_attn_workspace_size() bytes) when that size is non-zero. The caller
  * owns it; its contents need not be initialised. Calls that share one
  * workspace must not overlap.
+ *
+ * ws_counters_zero: the BALANCED schedule's arrival counters must be zero
+ * when the attention kernel starts, and every completed call leaves them
+ * zero. With 0 the call clears them (inside the Q/K pre-pass when one runs,
+ * else with one small fill kernel). With 1 the caller guarantees they are
+ * zero because the workspace comes unchanged from an earlier completed call
+ * with the same arguments, and the clear is skipped.
  *
  * schedule: a dit_schedule value (0 = AUTO).
  *
@@ -127,7 +144,7 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * softmax runs over all real keys of all segments; pad query rows get O = +0
  * and LSE = -inf. s must be a multiple of its segment length and valid <=
  * segment length (else DIT_ERR_INVALID); kv_seg_len must be a multiple of 64
- * and the schedule not BALANCED (else DIT_ERR_UNSUPPORTED).
+ * (segmented calls run PER_QTILE whatever the schedule asks).
  *
  * fixed_m = 1 (the fixed-m softmax of maxdiffusion PR #491; the bound is not
  * printed there, the plain reading is used): before the attention kernel,
@@ -138,8 +155,8 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * have 2 sm_scale |q_i| R <= 96 ln 2 uses m_i as its fixed softmax maximum
  * (no running max, no rescale); any other q-tile keeps the online softmax.
  * Results agree with the online softmax to rounding and are reproducible
- * run to run. Needs workspace; not with the BALANCED schedule
- * (DIT_ERR_UNSUPPORTED). It pays for itself only on long key ranges.
+ * run to run. Needs workspace; runs PER_QTILE whatever the schedule asks. It
+ * pays for itself only on long key ranges.
  */
 typedef struct dit_attn_desc {
   int32_t B, H, d;               /* d in {64, 128}, else DIT_ERR_UNSUPPORTED */
@@ -160,17 +177,19 @@ typedef struct dit_attn_desc {
   float norm_eps;
   int32_t q_seg_len, kv_seg_len; /* 0, or segment length: see "Segments" above */
   int32_t fixed_m;               /* 0 = online softmax, 1 = fixed-m: see above */
+  int32_t ws_counters_zero;      /* 1: the workspace's Stream-K counters are known zero; see above */
 } dit_attn_desc;
 
 /* Bytes of workspace dit_attn_fwd needs for `desc` (0 when neither Q nor K
  * is rotated or normalised, the schedule needs no partial results and
- * fixed_m is 0, or when kv_valid is 0). Under BALANCED the size depends on
- * the current device's compute-unit count (DIT_ERR_HIP if it cannot be
- * queried). */
+ * fixed_m is 0, or when kv_valid is 0). Under BALANCED and AUTO the schedule
+ * and the size depend on the current device's compute-unit count
+ * (DIT_ERR_HIP if it cannot be queried). */
 DIT_API int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes);
 
 /* Attention forward with fused RoPE and exact pad-key masking; see above. */
 DIT_API int dit_attn_fwd(const dit_attn_desc *desc, void *stream);
+
 
 /*
  * Merge n_parts partial results over disjoint key shards of the same queries

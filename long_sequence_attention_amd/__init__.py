@@ -68,7 +68,8 @@ def plan_padding(s_valid: int, multiple: int) -> int:
 
 
 def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule=0,
-               q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False):
+               q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False,
+               ws_counters_zero=False):
     B, H, s_q, d = q.shape
     desc = N.AttnDesc()
     desc.B, desc.H, desc.d = B, H, d
@@ -92,6 +93,7 @@ def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, sch
     desc.norm_eps = float(norm_eps)
     desc.q_seg_len, desc.kv_seg_len = int(q_seg_len), int(kv_seg_len)
     desc.fixed_m = 1 if fixed_m else 0
+    desc.ws_counters_zero = 1 if ws_counters_zero else 0
     return desc
 
 
@@ -110,18 +112,23 @@ def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, ro
 
 def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
              out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None, schedule=0,
-             q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False):
+             q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False,
+             ws_counters_zero=False):
     """Attention forward (dit_attn_fwd).
 
     q: [B, H, s_q, d], k/v: [B, H, s_kv, d] bf16 device tensors, any strides
     with d contiguous (e.g. a permuted [B, S, H, d] buffer). Rows >= q_valid /
     kv_valid are tail pads. rope_q / rope_k: (cos, sin) fp32 [S, d/2] tables
-    or None. schedule: 0 auto, 1 one workgroup per query tile, 2 balanced.
+    or None. schedule: 0 auto, 1 one workgroup per query tile, 2 balanced
+    (Stream-K: one workgroup per compute unit).
     q_norm / k_norm: fp32 [d] RMSNorm weights (per-head q/k RMS normalisation
     before RoPE, epsilon norm_eps) or None. q_seg_len / kv_seg_len > 0: the
     rows form segments of that length, each padded at its own tail, and
     q_valid / kv_valid count the real rows of each segment. fixed_m: use the
     a-priori row-max bound where it is tight enough (dit_attn_desc.fixed_m).
+    ws_counters_zero: the caller's `workspace` comes unchanged from an earlier
+    completed call with the same arguments, so its schedule counters are
+    already zero and the call skips clearing them.
     Returns (O, LSE) with O [B, H, s_q, d] in out_dtype (or `out`) and LSE
     fp32 [B, H, s_q] (natural log), or O alone if return_lse=False.
     """
@@ -158,8 +165,10 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
             _need_cuda(name, wt, torch.float32)
             if wt.shape != (d,) or not wt.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous fp32 [{d}] tensor")
+    if ws_counters_zero and workspace is None:
+        raise ValueError("ws_counters_zero needs the caller's workspace")
     desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule, q_norm, k_norm,
-                      norm_eps, q_seg_len, kv_seg_len, fixed_m)
+                      norm_eps, q_seg_len, kv_seg_len, fixed_m, ws_counters_zero)
     need = ctypes.c_size_t()
     with torch.cuda.device(q.device):
         N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")

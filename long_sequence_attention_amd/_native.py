@@ -54,6 +54,7 @@ class AttnDesc(ctypes.Structure):
         ("norm_eps", ctypes.c_float),
         ("q_seg_len", ctypes.c_int32), ("kv_seg_len", ctypes.c_int32),
         ("fixed_m", ctypes.c_int32),
+        ("ws_counters_zero", ctypes.c_int32),
     ]
 
 

@@ -2,6 +2,7 @@
 // geometry and status codes. Declarations and contracts: include/dit_attn.h.
 #include "dit_attn.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -77,11 +78,9 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   if (d->kv_seg_len > 0 && d->kv_seg_len % dit::kAttnBlockN != 0)
     return fail(DIT_ERR_UNSUPPORTED, "kv_seg_len=%d must be a multiple of the %d-row key tile", d->kv_seg_len,
                 dit::kAttnBlockN);
-  if (d->kv_seg_len > 0 && d->schedule == DIT_SCHED_BALANCED)
-    return fail(DIT_ERR_UNSUPPORTED, "the balanced schedule does not cover key segments");
   if (d->fixed_m != 0 && d->fixed_m != 1) return fail(DIT_ERR_INVALID, "fixed_m=%d must be 0 or 1", d->fixed_m);
-  if (d->fixed_m && d->schedule == DIT_SCHED_BALANCED)
-    return fail(DIT_ERR_UNSUPPORTED, "the balanced schedule does not cover the fixed-m softmax");
+  if (d->ws_counters_zero != 0 && d->ws_counters_zero != 1)
+    return fail(DIT_ERR_INVALID, "ws_counters_zero=%d must be 0 or 1", d->ws_counters_zero);
   if (d->o_dtype != DIT_BF16 && d->o_dtype != DIT_F32) return fail(DIT_ERR_INVALID, "o_dtype=%d is not a dit_dtype", d->o_dtype);
   if (d->s_q > 0 && (d->q == nullptr || d->o == nullptr)) return fail(DIT_ERR_INVALID, "q and o must be non-NULL when s_q > 0");
   if (d->kv_valid > 0 && (d->k == nullptr || d->v == nullptr))
@@ -128,7 +127,8 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
 struct AttnPlan {
   size_t k_bytes = 0;       // prepared (normalised / rotated) K, dense [B, H, s_kv, d] bf16
   size_t q_bytes = 0;       // prepared Q, dense [B, H, s_q, d] bf16 (after K)
-  int splits = 1;           // key-split pieces per q-tile (1 = one workgroup per q-tile)
+  int sk_grid = 0;          // split-schedule workgroups (0 = one workgroup per q-tile)
+  int sk_main = 0, sk_kc = 0;
   size_t part_o_off = 0, part_l_off = 0, count_off = 0;
   int64_t n_counts = 0;
   // fixed-m statistics (fm = false: online softmax)
@@ -140,16 +140,58 @@ struct AttnPlan {
 
 constexpr int kBlockM = dit::kAttnBlockM, kBlockN = dit::kAttnBlockN, kThreads = dit::kAttnThreads;
 
-// Estimated run time, in key tiles of one workgroup, of nq q-tiles over nk
-// key tiles cut into S pieces each on `slots` resident workgroups: whole
-// rounds of slots times the longest piece, plus 5% for the partials and the
-// merge when S > 1.
-double split_cost(int64_t nq, int64_t nk, int64_t S, int64_t slots) {
-  const int64_t rounds = (nq * S + slots - 1) / slots;
-  const int64_t piece = (nk + S - 1) / S;
-  return (double)(rounds * piece) * (S > 1 ? 1.05 : 1.0);
+// Split schedule for nq q-tiles of nk key tiles on `cus` compute units
+// (one workgroup per CU). When the q-tiles fill less than one wave
+// (nq < cus): nq main workgroups run keys [0, kc) of their q-tile in step
+// and the cus - nq spare CUs split the remaining key tails evenly; kc is
+// chosen so that a main workgroup's kc tiles match a helper's share of the
+// tails plus kPieceCost tile-steps for the helper's extra Q loads and
+// partial stores. Otherwise (or when that leaves no tail) plain Stream-K
+// over all units.
+constexpr int64_t kPieceCost = 4;
+struct SplitPlan {
+  int grid = 0, main = 0, kc = 0;
+};
+SplitPlan split_plan(int64_t nq, int64_t nk, int64_t cus) {
+  SplitPlan sp;
+  if (nq < cus && nk >= 2) {
+    int64_t helpers = cus - nq;
+    int64_t kc = (nq * nk + helpers * kPieceCost + cus - 1) / cus;
+    kc = kc < 1 ? 1 : (kc > nk - 1 ? nk - 1 : kc);
+    const int64_t tail_units = nq * (nk - kc);
+    if (helpers > tail_units) helpers = tail_units;
+    sp.grid = (int)(nq + helpers);
+    sp.main = (int)nq;
+    sp.kc = (int)kc;
+  } else {
+    const int64_t units = nq * nk;
+    sp.grid = (int)(units < cus ? units : cus);
+  }
+  return sp;
 }
+// AUTO never takes the split: on MI355X it measured slower on every shape
+// tried. The chip is power-limited, so the shader clock falls from about
+// 1.9 GHz with the Wan 480p shard's 190 q-tiles to about 1.65 GHz with every
+// CU busy, which cancels most of the shorter key range; and each piece's
+// device-scope partial store (3.5-6 us) and merge (about 9 us) cost more
+// than the rest saves (Wan 480p: 144 against 112 us per kernel).
+bool split_pays(int64_t, int64_t, int64_t) { return false; }
 
+// Compute units of the current device, or 0 when it cannot be queried (AUTO
+// then keeps one workgroup per q-tile). Cached per device id.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   AttnPlan p;
   if ((d->cos_k != nullptr || d->k_norm_w != nullptr) && d->kv_valid > 0)
@@ -160,36 +202,26 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   const int64_t nk = (d->kv_valid + kBlockN - 1) / kBlockN;
   if (d->schedule < DIT_SCHED_AUTO || d->schedule > DIT_SCHED_BALANCED)
     return fail(DIT_ERR_INVALID, "schedule=%d is not a dit_schedule", d->schedule);
-  // AUTO resolves to one workgroup per q-tile: on MI355X the key-split
-  // schedule measures slower on the Wan, FLUX and HunyuanVideo shapes (each
-  // piece pays a prologue, partial writes and a merge, its L2 reuse is
-  // lower and the clock drops with every CU busy), so it runs only when
-  // asked for.
-  if (d->schedule == DIT_SCHED_BALANCED && nq > 0 && nk >= 2) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+  // the split schedule covers plain (one-segment, online-softmax) calls with
+  // at least two key tiles when BALANCED asks for it (see split_pays for AUTO)
+  if (d->schedule != DIT_SCHED_PER_QTILE && nq > 0 && nk >= 2 && d->kv_seg_len == 0 && !d->fixed_m) {
+    const int cus = device_cus();
+    if (cus <= 0 && d->schedule == DIT_SCHED_BALANCED)
       return fail(DIT_ERR_HIP, "cannot query the compute-unit count of the current device");
-    const int64_t slots = (int64_t)(512 / dit::kAttnThreads) * cus;   // workgroups resident per CU (two waves per SIMD)
-    // the best split of at most 8 pieces (pieces of at least 2 key tiles)
-    int64_t best = 1;
-    double best_cost = split_cost(nq, nk, 1, slots);
-    for (int64_t S = 2; S <= 8 && 2 * S <= nk; ++S) {
-      const double c = split_cost(nq, nk, S, slots);
-      if (c < best_cost || best == 1) {
-        best = S;
-        best_cost = c;
-      }
+    if (cus > 0 && (d->schedule == DIT_SCHED_BALANCED || split_pays(nq, nk, cus))) {
+      const SplitPlan sp = split_plan(nq, nk, cus);
+      p.sk_grid = sp.grid;
+      p.sk_main = sp.main;
+      p.sk_kc = sp.kc;
     }
-    if (nq * best > 0x7fffffffLL) best = 1;
-    p.splits = (int)best;
   }
   size_t off = p.k_bytes + p.q_bytes;
-  if (p.splits > 1) {
-    const size_t pieces = (size_t)nq * p.splits;
+  if (p.sk_grid > 0) {
+    const size_t slots = 2 * (size_t)p.sk_grid;
     p.part_o_off = off;
-    off += round_up(pieces * kThreads * (d->d / 2) * sizeof(float), 256);
+    off += round_up(slots * kThreads * (d->d / 2) * sizeof(float), 256);
     p.part_l_off = off;
-    off += round_up(pieces * kBlockM * sizeof(float), 256);
+    off += round_up(slots * kBlockM * sizeof(float), 256);
     p.count_off = off;
     p.n_counts = nq;
     off += round_up((size_t)nq * sizeof(int32_t), 256);
@@ -281,14 +313,28 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
   p.o_f32 = d.o_dtype == DIT_F32;
   p.n_qtiles = (d.s_q + dit::kAttnBlockM - 1) / dit::kAttnBlockM;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.sk_grid = pl.sk_grid;
+  p.sk_main = pl.sk_main;
+  p.sk_kc = pl.sk_kc;
+  if (pl.sk_grid > 0) {
+    char *ws = static_cast<char *>(d.workspace);
+    p.sk_part_o = reinterpret_cast<float *>(ws + pl.part_o_off);
+    p.sk_part_l = reinterpret_cast<float *>(ws + pl.part_l_off);
+    p.sk_count = reinterpret_cast<int32_t *>(ws + pl.count_off);
+  }
 
   // one pre-pass normalises and / or rotates K (valid rows) and Q (all rows)
-  // into the workspace
-  if (pl.k_bytes + pl.q_bytes > 0) {
+  // into the workspace, and clears the split schedule's arrival counters
+  const bool prepass = pl.k_bytes + pl.q_bytes > 0;
+  if (prepass) {
     dit::RopeRotateParams r{};
     char *ws = static_cast<char *>(d.workspace);
     r.B = d.B; r.H = d.H; r.d = d.d;
     r.eps = d.norm_eps;
+    if (!d.ws_counters_zero) {
+      r.zero = p.sk_count;
+      r.n_zero = (int32_t)pl.n_counts;
+    }
     if (pl.k_bytes > 0) {
       dit::RopeSeg &g = r.seg[r.n_seg++];
       g.x = p.k; g.y = reinterpret_cast<dit::bf16_t *>(ws);
@@ -330,12 +376,7 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
     p.fm_m = f.m;
     p.fm_ok = f.ok;
   }
-  p.sk_splits = pl.splits;
-  if (pl.splits > 1) {
-    char *ws = static_cast<char *>(d.workspace);
-    p.sk_part_o = reinterpret_cast<float *>(ws + pl.part_o_off);
-    p.sk_part_l = reinterpret_cast<float *>(ws + pl.part_l_off);
-    p.sk_count = reinterpret_cast<int32_t *>(ws + pl.count_off);
+  if (pl.sk_grid > 0 && !prepass && !d.ws_counters_zero) {
     // arrival counters start at zero (a fill kernel, not a memset node)
     rc = hip_status(dit::launch_zero_i32(p.sk_count, pl.n_counts, st), "counter clear launch");
     if (rc != DIT_OK) return rc;

@@ -532,11 +532,12 @@ __device__ __forceinline__ void store_final(const P &p, int b, int h, int qrow, 
 
 // Partials of split q-tiles move between workgroups that may sit on
 // different XCDs (separate L2s), so they are written and read with the
-// agent-coherent cache policy (sc1) instead of through a fence that would
-// write back a whole L2. Slot s holds 256 threads x (d/8) float4 of O / l,
-// stored chunk-major so one wave instruction covers 1 KB contiguously, and
-// 128 floats of log2 LSE.
-constexpr int kSC1 = 16;   // buffer cache-policy bit: agent-coherent access
+// device-scope cache policy (sc1): such a store is complete at the device's
+// coherence point once vmcnt reaches zero, and such a load is served from
+// it, so no whole-L2 writeback or invalidate is needed. Slot s holds 512
+// threads x (d/8) float4 of O / l, stored chunk-major so one wave
+// instruction covers 1 KB contiguously, and 256 floats of log2 LSE.
+constexpr int kSC1 = 16;   // buffer cache-policy bit: device scope
 
 template <int D, class P>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_o_view(const P &p, int slot) {
@@ -551,59 +552,173 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_l_view(const P &p, int sl
                                            0x00020000);
 }
 
-// The last piece of q-tile T to finish combines all S pieces (slot T*S + s
-// holds piece s; this workgroup's own piece `own` is still in registers as
-// the normalised o = acc / l with log2 LSE lse2) and writes the final O and
-// LSE: O = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - M), M = max_s
-// lse_s. The pieces are combined in key order whichever finished last, so
-// the result is the same bits on every call.
-template <int D, class P>
-__device__ __forceinline__ void merge_pieces(const P &p, const Lane<D> &ln, int T, int own, int b, int h, int qrow,
-                                             bool row_ok, const f32x16 *o, float lse2) {
-  constexpr int DB = D / 32;
-  const int S = p.sk_splits;
-  const int row = ln.wave * 32 + ln.l32;
-  float M = -INFINITY;
-  for (int x = 0; x < S; ++x) {
-    const float lx = x == own ? lse2
-                              : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, T * S + x), row * 4,
-                                                                                    0, kSC1));
-    M = fmaxf(M, lx);
+// Split-schedule geometry ("data-parallel + Stream-K tail"). With M > 0,
+// main workgroup T < M (= the number of q-tiles) runs keys [0, kc) of
+// q-tile T, all of them in step so each K/V tile is read while it is in L2;
+// the H helper workgroups split the remaining tails [kc, nk) of all q-tiles,
+// flattened q-tile major into U = nq (nk - kc) units, into equal contiguous
+// ranges (helper h owns [h U / H, (h+1) U / H)). With M = 0 and kc = 0 this
+// is plain Stream-K over every unit. Partial-result slots: main T uses slot
+// T; helper slots as in helper_slot.
+struct SkGeo {
+  int64_t U;
+  int M, H, nk, kc;
+  __device__ int nt() const { return nk - kc; }
+  __device__ int64_t start(int h) const { return (int64_t)h * U / H; }
+  // the helper whose range holds tail unit u
+  __device__ int owner(int64_t u) const { return (int)(((u + 1) * H - 1) / U); }
+  __device__ int helper_slot(int h, int T) const {
+    // with main workgroups, a helper's middle q-tiles are pieces too: slot
+    // M + h + T is unique (helper h's q-tiles start at or after helper
+    // h-1's last) and below M + H + nq <= 2 grid; without them (plain
+    // Stream-K) a middle q-tile is whole and two slots per helper suffice
+    return M > 0 ? M + h + T : 2 * h + ((int)(start(h) / nt()) == T ? 0 : 1);
   }
-  float wsum = 0.f;
-  for (int x = 0; x < S; ++x) {
-    wsum += __builtin_amdgcn_exp2f(
-        (x == own ? lse2
-                  : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, T * S + x), row * 4, 0, kSC1))) -
-        M);
-  }
-  // one 32-channel block at a time: the running sum of the pieces before
-  // this workgroup's own one needs only 16 registers
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    f32x16 a = f32x16{};
-    for (int x = 0; x < S; ++x) {
-      if (x == own) {
-        const float wx = __builtin_amdgcn_exp2f(lse2 - M);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) a[r] = fmaf(wx, o[db][r], a[r]);
-      } else {
-        const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, T * S + x);
-        const float wx = __builtin_amdgcn_exp2f(
-            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, T * S + x), row * 4, 0, kSC1)) - M);
-        u32x4 c[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(v, ln.tid * 16, (db * 4 + i) * NT * 16, kSC1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[4 * i + e] = fmaf(wx, __uint_as_float(c[i][e]), a[4 * i + e]);
-      }
+  // q-tile T's pieces in key order: piece 0 is the main workgroup's (when
+  // M > 0), then the helpers h_lo(T)..h_hi(T)
+  __device__ int h_lo(int T) const { return owner((int64_t)T * nt()); }
+  __device__ int h_hi(int T) const { return owner((int64_t)(T + 1) * nt() - 1); }
+  __device__ int n_pieces(int T) const { return (M > 0 ? 1 : 0) + h_hi(T) - h_lo(T) + 1; }
+  __device__ int slot_of_piece(int T, int x) const {
+    if (M > 0) {
+      if (x == 0) return T;
+      --x;
     }
-    acc[db] = a;
+    return helper_slot(h_lo(T) + x, T);
   }
-  store_final<D>(p, b, h, qrow, ln.hf, acc, M + __log2f(wsum), row_ok ? 1.0f / wsum : 0.f, row_ok);
+};
+
+// Store this workgroup's piece of q-tile T (o = acc / l, normalised, and
+// its log2 LSE) into `slot`, device-scope.
+template <int D, class P>
+__device__ __forceinline__ void store_piece(const P &p, const Lane<D> &ln, int slot, const f32x16 *o, float lse2) {
+  constexpr int DB = D / 32;
+  const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, slot);
+#pragma unroll
+  for (int j = 0; j < DB * 4; ++j) {
+    const int db = j >> 2, r = 4 * (j & 3);
+    const u32x4 c = {__float_as_uint(o[db][r]), __float_as_uint(o[db][r + 1]), __float_as_uint(o[db][r + 2]),
+                     __float_as_uint(o[db][r + 3])};
+    __builtin_amdgcn_raw_buffer_store_b128(c, v, ln.tid * 16, j * NT * 16, kSC1);
+  }
+  if (ln.hf == 0)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), part_l_view(p, slot), (ln.wave * 32 + ln.l32) * 4, 0,
+                                          kSC1);
+}
+
+// The last piece of q-tile T to finish combines its n pieces (this
+// workgroup's own piece, index `own`, is still in registers as the
+// normalised o = acc / l with log2 LSE lse2; o is overwritten) and writes
+// the final O and LSE: O = sum_s w_s o_s / sum_s w_s with
+// w_s = 2^(lse_s - M), M = max_s lse_s, summed in key order whichever piece
+// finished last, so the result is the same bits on every call. Up to
+// kFastPieces pieces the loads are batched (every LSE at once; the other
+// pieces' share of one 32-channel block at once), so the merge costs one
+// memory round trip per 32-channel block plus one; beyond that a plain loop.
+constexpr int kFastPieces = 4;
+
+template <int D, class P>
+__device__ __forceinline__ void merge_pieces(const P &p, const Lane<D> &ln, const SkGeo &sk, int T, int own, int b,
+                                             int h, int qrow, bool row_ok, f32x16 *o, float lse2) {
+  constexpr int DB = D / 32;
+  constexpr int KO = kFastPieces - 1;   // other pieces on the fast path
+  const int row = ln.wave * 32 + ln.l32;
+  const int n = sk.n_pieces(T);
+  float M = lse2, wsum = 0.f;
+  if (n <= kFastPieces) {
+    // the other pieces in key order: oth[k] is piece x_k (k < n - 1)
+    int slot[KO];
+    float lx[KO], wx[KO];
+#pragma unroll
+    for (int k = 0; k < KO; ++k) {
+      const int x = k < own ? k : k + 1;
+      slot[k] = k < n - 1 ? sk.slot_of_piece(T, x) : 0;
+      lx[k] = k < n - 1 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, slot[k]), row * 4, 0,
+                                                                              kSC1))
+                        : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < KO; ++k) M = fmaxf(M, lx[k]);
+    const float w_own = __builtin_amdgcn_exp2f(lse2 - M);
+    // the sum of weights in key order: pieces before own, own, after own
+    for (int x = 0; x < n; ++x) {
+      const int k = x < own ? x : x - 1;
+      float w = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KO; ++kk) w = kk == k ? __builtin_amdgcn_exp2f(lx[kk] - M) : w;
+      wsum += x == own ? w_own : w;
+    }
+#pragma unroll
+    for (int k = 0; k < KO; ++k) wx[k] = k < n - 1 ? __builtin_amdgcn_exp2f(lx[k] - M) : 0.f;
+    auto load_block = [&](int db, u32x4 (&c)[KO][4]) {
+#pragma unroll
+      for (int k = 0; k < KO; ++k) {
+        if (k < n - 1) {
+          const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, slot[k]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            c[k][i] = __builtin_amdgcn_raw_buffer_load_b128(v, ln.tid * 16, (db * 4 + i) * NT * 16, kSC1);
+        }
+      }
+    };
+    u32x4 cur[KO][4];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      load_block(db, cur);
+      f32x16 a = f32x16{};
+      // key order: the other pieces before own, own, the ones after
+      for (int x = 0; x < n; ++x) {
+        if (x == own) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a[r] = fmaf(w_own, o[db][r], a[r]);
+        } else {
+          const int k = x < own ? x : x - 1;
+#pragma unroll
+          for (int kk = 0; kk < KO; ++kk) {
+            if (kk == k) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[4 * i + e] = fmaf(wx[kk], __uint_as_float(cur[kk][i][e]), a[4 * i + e]);
+            }
+          }
+        }
+      }
+      o[db] = a;
+    }
+  } else {
+    auto lse_of = [&](int x) {
+      return x == own ? lse2
+                      : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_view(p, sk.slot_of_piece(T, x)),
+                                                                             row * 4, 0, kSC1));
+    };
+    M = -INFINITY;
+    for (int x = 0; x < n; ++x) M = fmaxf(M, lse_of(x));
+    for (int x = 0; x < n; ++x) wsum += __builtin_amdgcn_exp2f(lse_of(x) - M);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f32x16 a = f32x16{};
+      for (int x = 0; x < n; ++x) {
+        const float w = __builtin_amdgcn_exp2f(lse_of(x) - M);
+        if (x == own) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a[r] = fmaf(w, o[db][r], a[r]);
+        } else {
+          const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, sk.slot_of_piece(T, x));
+          u32x4 c[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            c[i] = __builtin_amdgcn_raw_buffer_load_b128(v, ln.tid * 16, (db * 4 + i) * NT * 16, kSC1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[4 * i + e] = fmaf(w, __uint_as_float(c[i][e]), a[4 * i + e]);
+        }
+      }
+      o[db] = a;
+    }
+  }
+  store_final<D>(p, b, h, qrow, ln.hf, o, M + __log2f(wsum), row_ok ? 1.0f / wsum : 0.f, row_ok);
 }
 
 // Per-lane constants: wave / lane ids, the DMA source offsets and the
@@ -647,7 +762,7 @@ __device__ __forceinline__ void make_lane(const P &p, int tid, Lane<D> &ln) {
   }
 }
 
-template <int D, bool BALANCED>
+template <int D, bool STREAMK>
 __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   using G = Geo<D>;
   constexpr int DB = D / 32;
@@ -662,7 +777,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   f32x16 acc_o[DB];
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (!BALANCED) {
+  if (!STREAMK) {
     // one workgroup per q-tile, all key tiles
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int qt = logical % p.n_qtiles;
@@ -685,49 +800,76 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
     return;
   }
 
-  // ---- key-split schedule: piece s of q-tile T covers key tiles
-  // [s*nk/S, (s+1)*nk/S). Blocks are numbered split-major, so the pieces
-  // running together read the same key range (their K/V tiles stay in L2),
-  // and consecutive q-tiles of a head share an XCD. The last piece of a
-  // q-tile to finish merges the others with its own.
+  // ---- split schedule (geometry in SkGeo): a main workgroup runs one
+  // piece, a helper the pieces of its range in order. A piece covering a
+  // whole q-tile writes the final result; any other piece writes its
+  // partial (device scope) and, once every thread's stores have completed,
+  // bumps the q-tile's arrival counter; the piece that arrives last merges
+  // all pieces. Logical workgroups are contiguous per XCD, so the main
+  // workgroups of one head (one K/V) share an XCD's L2.
   const int nq_all = p.n_qtiles * p.H * p.B;
-  const int S = p.sk_splits;
-  const int s = blockIdx.x / nq_all;
-  const int T = xcd_remap(blockIdx.x - s * nq_all, nq_all);
-  const int kb = (int)((int64_t)s * nk / S), ke = (int)((int64_t)(s + 1) * nk / S);
-  const int qt = T % p.n_qtiles, bh = T / p.n_qtiles;
-  const int h = bh % p.H, b = bh / p.H;
-  const int qrow = qt * BM + ln.wave * 32 + ln.l32;
-  run_qtile<D>(p, smem, ln, b, h, qt, kb, ke, acc_o, m_run, l_run);
-  const float l_tot = pair_sum(l_run);
-  const float lse2 = m_run + __log2f(l_tot);
-  const bool row_ok = query_is_real(p, qrow);
-  // partial: O / l (fp32, in this lane's accumulator layout) and log2 LSE,
-  // written agent-coherent; the arrival counter is bumped once every
-  // thread's stores completed.
-  const int slot = T * S + s;
-  const float inv = 1.0f / l_tot;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc_o[db] *= inv;
-  const __amdgpu_buffer_rsrc_t v = part_o_view<D>(p, slot);
-#pragma unroll
-  for (int j = 0; j < DB * 4; ++j) {
-    const int db = j >> 2, r = 4 * (j & 3);
-    const u32x4 c = {__float_as_uint(acc_o[db][r]), __float_as_uint(acc_o[db][r + 1]),
-                     __float_as_uint(acc_o[db][r + 2]), __float_as_uint(acc_o[db][r + 3])};
-    __builtin_amdgcn_raw_buffer_store_b128(c, v, ln.tid * 16, j * NT * 16, kSC1);
+  const SkGeo sk{(int64_t)nq_all * (nk - p.sk_kc), p.sk_main, p.sk_grid - p.sk_main, nk, p.sk_kc};
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  int64_t u, u_end;
+  int hh = -1;   // helper index, or -1 for a main workgroup
+  if (g < sk.M) {
+    u = (int64_t)g * nk;   // main: q-tile g, keys [0, kc)
+    u_end = u + sk.kc;
+  } else {
+    hh = g - sk.M;
+    u = sk.start(hh);
+    u_end = sk.start(hh + 1);
   }
-  if (ln.hf == 0)
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), part_l_view(p, slot), (ln.wave * 32 + ln.l32) * 4, 0, kSC1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial is in coherent memory
-  __syncthreads();
-  if (ln.tid == 0) {
-    const int old = __hip_atomic_fetch_add(p.sk_count + T, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (old == S - 1) ? 1 : 0;
-    if (last_flag) __hip_atomic_store(p.sk_count + T, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (u < u_end) {
+    int T, kb, ke;
+    if (hh < 0) {
+      T = g;
+      kb = 0;
+      ke = sk.kc;
+    } else {
+      T = (int)(u / sk.nt());
+      kb = sk.kc + (int)(u - (int64_t)T * sk.nt());
+      ke = (int)((int64_t)kb + (u_end - u) < nk ? (int64_t)kb + (u_end - u) : nk);
+    }
+    const int qt = T % p.n_qtiles, bh = T / p.n_qtiles;
+    const int h = bh % p.H, b = bh / p.H;
+    const int qrow = qt * BM + ln.wave * 32 + ln.l32;
+    run_qtile<D>(p, smem, ln, b, h, qt, kb, ke, acc_o, m_run, l_run);
+    const float l_tot = pair_sum(l_run);
+    const float lse2 = m_run + __log2f(l_tot);
+    const bool row_ok = query_is_real(p, qrow);
+    if (kb == 0 && ke == nk) {
+      store_final<D>(p, b, h, qrow, ln.hf, acc_o, lse2, row_ok ? 1.0f / l_tot : 0.f, row_ok);
+    } else {
+      const float inv = 1.0f / l_tot;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] *= inv;
+      const int own = hh < 0 ? 0 : (sk.M > 0 ? 1 : 0) + hh - sk.h_lo(T);
+      const int np = sk.n_pieces(T);
+      // if every other piece has already arrived (each publishes before it
+      // counts itself), this one is last: merge without publishing
+      if (ln.tid == 0) {
+        const int seen = __hip_atomic_load(p.sk_count + T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = seen == np - 1 ? 1 : 0;
+        if (last_flag) __hip_atomic_store(p.sk_count + T, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (!last_flag) {
+        store_piece<D>(p, ln, sk.slot_of_piece(T, own), acc_o, lse2);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's piece is at the coherence point
+        __syncthreads();                      // ... and every other thread's (and last_flag was read)
+        if (ln.tid == 0) {
+          const int old = __hip_atomic_fetch_add(p.sk_count + T, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last_flag = (old == np - 1) ? 1 : 0;
+          if (last_flag) __hip_atomic_store(p.sk_count + T, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+      }
+      if (last_flag) merge_pieces<D>(p, ln, sk, T, own, b, h, qrow, row_ok, acc_o, lse2);
+    }
+    u += ke - kb;
+    __syncthreads();   // every wave is done with this piece's LDS tiles and last_flag
   }
-  __syncthreads();
-  if (last_flag) merge_pieces<D>(p, ln, T, s, b, h, qrow, row_ok, acc_o, lse2);
 }
 
 // Keys in n_kv_seg segments of kv_seg_len rows (a multiple of the key tile),
@@ -789,12 +931,16 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_seg_kernel(AttnParams p
 // kRopeHeads (b, h) pairs (blockIdx.z picks the group), so the tables are
 // read once per row and head group rather than once per head. The RMS of a
 // head vector is summed over the RUNS = d/16 consecutive lanes of its row.
+// The first workgroup also clears the Stream-K arrival counters of the
+// attention launch that follows (saving that launch a clearing kernel).
 constexpr int kRopeHeads = 4;
 
 template <int RUNS>
 __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
   constexpr int ROWS = 256 / RUNS, HALF = RUNS * 8;
   const RopeSeg &g = p.seg[blockIdx.y];
+  if (p.zero != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < p.n_zero; i += 256) p.zero[i] = 0;
   const int c = threadIdx.x % RUNS;
   const int nbh = p.B * p.H;
   const int bh0 = blockIdx.z * kRopeHeads;
@@ -882,14 +1028,14 @@ hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream) {
     else hipLaunchKernelGGL(attn_fwd_seg_kernel<64>, dim3((unsigned)nb), dim3(NT), 0, stream, p);
     return hipGetLastError();
   }
-  const bool bal = p.sk_splits > 1;
-  const int64_t nblocks = (int64_t)p.n_qtiles * p.H * p.B * (bal ? p.sk_splits : 1);
+  const bool sk = p.sk_grid > 0;
+  const int64_t nblocks = sk ? p.sk_grid : (int64_t)p.n_qtiles * p.H * p.B;
   if (nblocks <= 0) return hipSuccess;
   if (d == 128) {
-    if (bal) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
+    if (sk) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
     else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
   } else {
-    if (bal) hipLaunchKernelGGL((attn_fwd_kernel<64, true>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
+    if (sk) hipLaunchKernelGGL((attn_fwd_kernel<64, true>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
     else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), dim3((unsigned)nblocks), dim3(NT), 0, stream, p);
   }
   return hipGetLastError();
@@ -899,7 +1045,7 @@ hipError_t launch_rope_rotate(const RopeRotateParams &p, hipStream_t stream) {
   int rows = 0;
   for (int i = 0; i < p.n_seg; ++i) rows = p.seg[i].rows > rows ? p.seg[i].rows : rows;
   const int64_t nbh = (int64_t)p.B * p.H;
-  if (p.n_seg <= 0 || rows <= 0 || nbh <= 0) return hipSuccess;
+  if (p.n_seg <= 0 || rows <= 0 || nbh <= 0) return launch_zero_i32(p.zero, p.n_zero, stream);
   const int runs = p.d / 16;
   const int per_block = 256 / runs;
   int64_t bx = (rows + per_block - 1) / per_block;

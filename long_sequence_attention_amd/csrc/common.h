@@ -68,12 +68,13 @@ struct AttnParams {
   int32_t o_f32;
   int32_t n_qtiles;
   float scale_log2;  // sm_scale * log2(e)
-  // key-split schedule (sk_splits > 1): the keys of every q-tile are cut
-  // into sk_splits contiguous ranges, one workgroup each; pieces meet in the
-  // workspace below
-  int32_t sk_splits;
-  float *sk_part_o;  // [q-tiles * sk_splits][kAttnThreads][d/2] partial O / l, fp32
-  float *sk_part_l;  // [q-tiles * sk_splits][kAttnBlockM rows] partial LSE, log2 units
+  // split schedule (sk_grid > 0 workgroups): sk_main main workgroups (one
+  // per q-tile, keys [0, sk_kc)) and sk_grid - sk_main helpers splitting the
+  // remaining key tails Stream-K style (sk_main = sk_kc = 0: plain Stream-K
+  // over every unit); the pieces of a q-tile meet in the workspace below
+  int32_t sk_grid, sk_main, sk_kc;
+  float *sk_part_o;  // [sk_main + 2 helpers][kAttnThreads][d/2] partial O / l, fp32
+  float *sk_part_l;  // [sk_main + 2 helpers][kAttnBlockM rows] partial LSE, log2 units
   int32_t *sk_count; // [q-tiles] arrival counters, zero on entry (left zero on exit)
   // fixed-m softmax (fm_m != nullptr): row bounds [B*H][s_q] and per-q-tile
   // flags [B*H][n_qtiles] from launch_fixed_m
@@ -94,11 +95,15 @@ struct RopeSeg {
   int32_t S, rows;
 };
 
-// Parameters of the Q / K pre-pass (one launch for both tensors).
+// Parameters of the Q / K pre-pass (one launch for both tensors). zero /
+// n_zero: int32 words the launch also clears (the Stream-K arrival
+// counters of the attention launch that follows), or NULL / 0.
 struct RopeRotateParams {
   RopeSeg seg[2];
   int32_t n_seg, B, H, d;
   float eps;   // RMSNorm epsilon
+  int32_t *zero;
+  int32_t n_zero;
 };
 
 constexpr int kMaxMergeParts = 16;

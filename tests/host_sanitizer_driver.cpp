@@ -59,7 +59,7 @@ int main() {
     {"s_kv % kv_seg_len", [](dit_attn_desc &d) { d.kv_seg_len = 100; }, DIT_ERR_INVALID, "multiple of kv_seg_len"},
     {"kv_seg_len not tile", [](dit_attn_desc &d) { d.kv_seg_len = 32; d.kv_valid = 32; }, DIT_ERR_UNSUPPORTED, "key tile"},
     {"fixed_m = 2", [](dit_attn_desc &d) { d.fixed_m = 2; }, DIT_ERR_INVALID, "fixed_m"},
-    {"fixed_m balanced", [](dit_attn_desc &d) { d.fixed_m = 1; d.schedule = 2; }, DIT_ERR_UNSUPPORTED, "fixed-m"},
+    {"ws_counters_zero", [](dit_attn_desc &d) { d.ws_counters_zero = 3; }, DIT_ERR_INVALID, "ws_counters_zero"},
     {"schedule", [](dit_attn_desc &d) { d.schedule = 9; }, DIT_ERR_INVALID, "schedule"},
     {"misaligned q", [](dit_attn_desc &d) { d.q = reinterpret_cast<void *>(uintptr_t(0x10000008)); }, DIT_ERR_UNSUPPORTED, "16-byte aligned"},
     {"stride not x8", [](dit_attn_desc &d) { d.q_stride[0] = 256 * 2 * 128; d.q_stride[1] = 128; d.q_stride[2] = 132; }, DIT_ERR_UNSUPPORTED, "multiples of 8"},

@@ -81,10 +81,9 @@ def _desc(**kw):
     (dict(kv_seg_len=128, kv_valid=129), -1, b"kv_valid"),
     (dict(q_seg_len=128, q_valid=200), -1, b"q_valid"),
     (dict(kv_seg_len=32, kv_valid=32), -2, b"key tile"),
-    (dict(kv_seg_len=128, kv_valid=100, schedule=2), -2, b"balanced"),
     (dict(kv_seg_len=-1), -1, b"segment lengths"),
     (dict(fixed_m=2), -1, b"fixed_m"),
-    (dict(fixed_m=1, schedule=2), -2, b"fixed-m"),
+    (dict(ws_counters_zero=3), -1, b"ws_counters_zero"),
 ])
 def test_attn_fwd_rejects_bad_arguments_before_any_hip_call(L, kw, code, msg):
     d = _desc(**kw)

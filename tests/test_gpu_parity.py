@@ -333,7 +333,7 @@ def test_fixed_m_softmax_matches_oracle(ops, name):
     kw = dict(q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs)
     o1, l1 = ops.attn_fwd(qd, kd, vd, fixed_m=True, **kw)
     o2, l2 = ops.attn_fwd(qd, kd, vd, fixed_m=True, **kw)
-    o0, l0 = ops.attn_fwd(qd, kd, vd, **kw)
+    o0, l0 = ops.attn_fwd(qd, kd, vd, schedule=1, **kw)   # the online path of the same schedule
     torch.cuda.synchronize()
     O_ref, L_ref = oracle.dit_path(q, k, v, pos, pos, w.axes, w.theta, w.s_valid, w.s_valid)
     valid = np.arange(w.s_pad) < w.s_valid
@@ -390,7 +390,8 @@ def test_fixed_m_falls_back_to_online_for_a_loose_bound(ops):
     v = W.bf16_bits(r.standard_normal((1, 2, 512, 128)).astype(np.float32))
     qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
     o1, l1 = ops.attn_fwd(qd, kd, vd, q_valid=500, kv_valid=480, fixed_m=True)
-    o0, l0 = ops.attn_fwd(qd, kd, vd, q_valid=500, kv_valid=480)
+    # fixed-m runs one workgroup per q-tile: compare with that schedule
+    o0, l0 = ops.attn_fwd(qd, kd, vd, q_valid=500, kv_valid=480, schedule=1)
     torch.cuda.synchronize()
     assert np.array_equal(raw_bits(o1), raw_bits(o0)) and np.array_equal(raw_bits(l1), raw_bits(l0))
 
@@ -950,12 +951,17 @@ def test_pad_unpad_round_trip(ops):
 @pytest.mark.parametrize("case", [
     dict(name="tiny", sched=2),
     dict(name="hunyuan", sched=2),
+    dict(name="wan480", sched=2),
+    dict(name="flux", sched=2),
     dict(name="wan480", sched=1),
     dict(name="flux", sched=1),
 ])
 def test_forced_schedules_match_oracle(ops, case):
-    """Both work schedules (one workgroup per query tile; key ranges split
-    into pieces merged in the workspace) against the oracle."""
+    """Both work schedules against the oracle: one workgroup per query tile,
+    and the split (BALANCED) schedule, whose pieces meet in the workspace:
+    with fewer query tiles than CUs (tiny, HunyuanVideo, Wan 480p) main
+    workgroups plus helpers splitting the key tails, else (FLUX's 432 query
+    tiles) plain Stream-K over every unit."""
     import torch
     w = W.WORKLOADS[case["name"]]
     say(f"schedule {case['sched']} {w.name}")
@@ -974,7 +980,8 @@ def test_forced_schedules_match_oracle(ops, case):
 
 @pytest.mark.parametrize("kv_valid", [1000, 999, 129, 65])
 def test_balanced_schedule_edge_key_counts(ops, kv_valid):
-    """Balanced schedule with ragged key counts: pieces that end on the masked
+    """Split schedule with ragged key counts (a few query tiles, so each is
+    cut into many pieces: the merge's general path): pieces that end on the masked
     tail tile, single-tile pieces, and repeated calls reusing one workspace
     (arrival counters are reset by every call)."""
     import torch
