@@ -190,6 +190,29 @@ DIT_API int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes);
 /* Attention forward with fused RoPE and exact pad-key masking; see above. */
 DIT_API int dit_attn_fwd(const dit_attn_desc *desc, void *stream);
 
+/* Size of the static device scratch array behind dit_attn_fwd_noalloc. */
+#define DIT_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/*
+ * dit_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels as dit_attn_fwd with the same desc, but
+ * the workspace is a static device array of the library,
+ * DIT_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held from the library's load
+ * on that GPU until the process ends; desc->workspace, workspace_bytes and
+ * ws_counters_zero are ignored. The caller still owns and passes Q, K, V, O,
+ * LSE and the tables. Nothing is allocated or freed: the array's device
+ * address is looked up once per device (hipGetSymbolAddress, with the device
+ * current) and cached.
+ * A call whose workspace (dit_attn_workspace_size) exceeds the array returns
+ * DIT_ERR_UNSUPPORTED before any launch (e.g. the Wan 720p shard's 388 MB of
+ * rotated Q and K). Every call on one GPU uses the same array, which keeps
+ * the previous call's contents (the schedule counters are cleared by each
+ * call): calls that may overlap on one GPU (other streams, other threads)
+ * race on it and must be serialised by the caller. Status codes otherwise
+ * as dit_attn_fwd; DIT_ERR_HIP if the array's address cannot be resolved.
+ */
+DIT_API int dit_attn_fwd_noalloc(const dit_attn_desc *desc, void *stream);
 
 /*
  * Merge n_parts partial results over disjoint key shards of the same queries

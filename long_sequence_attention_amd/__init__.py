@@ -15,8 +15,10 @@ import torch
 from . import _native as N
 from ._native import DitError  # noqa: F401
 
-__all__ = ["attn_fwd", "lse_merge", "rope_split_tables", "pad_tokens", "unpad_tokens",
-           "plan_padding", "library_path", "attn_workspace_size"]
+__all__ = ["attn_fwd", "attn_fwd_noalloc", "lse_merge", "rope_split_tables", "pad_tokens", "unpad_tokens",
+           "plan_padding", "library_path", "attn_workspace_size", "NOALLOC_SCRATCH_BYTES"]
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # DIT_NOALLOC_SCRATCH_BYTES
 
 
 def library_path() -> str:
@@ -113,7 +115,7 @@ def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, ro
 def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
              out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None, schedule=0,
              q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False,
-             ws_counters_zero=False):
+             ws_counters_zero=False, _noalloc=False):
     """Attention forward (dit_attn_fwd).
 
     q: [B, H, s_q, d], k/v: [B, H, s_kv, d] bf16 device tensors, any strides
@@ -169,6 +171,10 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
         raise ValueError("ws_counters_zero needs the caller's workspace")
     desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule, q_norm, k_norm,
                       norm_eps, q_seg_len, kv_seg_len, fixed_m, ws_counters_zero)
+    if _noalloc:
+        with torch.cuda.device(q.device):
+            N.check(N.lib().dit_attn_fwd_noalloc(ctypes.byref(desc), _stream(q.device)), "attn_fwd_noalloc")
+        return (out, lse) if return_lse else out
     need = ctypes.c_size_t()
     with torch.cuda.device(q.device):
         N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")
@@ -185,6 +191,19 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
     with torch.cuda.device(q.device):
         N.check(N.lib().dit_attn_fwd(ctypes.byref(desc), _stream(q.device)), "attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def attn_fwd_noalloc(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
+                     out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, schedule=0,
+                     q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False):
+    """dit_attn_fwd_noalloc: attn_fwd with the library's static device scratch
+    (NOALLOC_SCRATCH_BYTES per GPU) as the workspace; the library allocates
+    nothing (pass `out` and `lse` to allocate nothing here either). Calls on
+    one GPU share the scratch and must not overlap."""
+    return attn_fwd(q, k, v, q_valid=q_valid, kv_valid=kv_valid, rope_q=rope_q, rope_k=rope_k, sm_scale=sm_scale,
+                    out=out, out_dtype=out_dtype, lse=lse, return_lse=return_lse, schedule=schedule, q_norm=q_norm,
+                    k_norm=k_norm, norm_eps=norm_eps, q_seg_len=q_seg_len, kv_seg_len=kv_seg_len, fixed_m=fixed_m,
+                    _noalloc=True)
 
 
 def lse_merge(o_parts, lse_parts, *, q_valid=None, out_dtype=torch.bfloat16, out=None, lse_out=None,

@@ -23,6 +23,7 @@ DIT_SCHED_BALANCED = 2
 EXPORTED = (
     "dit_attn_workspace_size",
     "dit_attn_fwd",
+    "dit_attn_fwd_noalloc",
     "dit_lse_merge",
     "dit_rope_split_tables",
     "dit_pad_tokens",
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     L.dit_attn_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)]
     L.dit_attn_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp]
+    L.dit_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnDesc), vp]
     L.dit_lse_merge.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, i32, i32, i32, i32,
                                 vp, i32, vp, vp]
     L.dit_rope_split_tables.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int32), i32, f32, vp, vp, vp]

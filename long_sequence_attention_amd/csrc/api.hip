@@ -10,6 +10,12 @@
 
 #include "common.h"
 
+// Workspace of dit_attn_fwd_noalloc: one copy per GPU the library runs on,
+// held until the process ends. Host code uses only the device address
+// that hipGetSymbolAddress returns for it (scratch_ptr below), never the
+// array's own name, which on the host is only a stand-in.
+static __device__ __align__(256) unsigned char scratch[DIT_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[1024];
@@ -247,6 +253,28 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   *pl = p;
   return DIT_OK;
 }
+// Device address of `scratch` on the current device, resolved once per
+// device (with that device current) and cached; NULL with the status in rc
+// when it cannot be resolved.
+void *scratch_ptr(int *rc) {
+  static std::atomic<void *> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *rc = fail(DIT_ERR_HIP, "no current HIP device (or device id beyond 63) for the static scratch");
+    return nullptr;
+  }
+  void *ptr = cache[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *rc = fail(DIT_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    cache[dev].store(ptr, std::memory_order_release);
+  }
+  *rc = DIT_OK;
+  return ptr;
+}
 }  // namespace
 
 extern "C" {
@@ -271,6 +299,28 @@ int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes) {
   if ((rc = plan_attn(desc, &pl)) != DIT_OK) return rc;
   *bytes = pl.total;
   return ok();
+}
+
+int dit_attn_fwd_noalloc(const dit_attn_desc *desc, void *stream) {
+  float scale;
+  int rc = validate_attn(desc, &scale);
+  if (rc != DIT_OK) return rc;
+  AttnPlan pl;
+  if ((rc = plan_attn(desc, &pl)) != DIT_OK) return rc;
+  if (pl.total > (size_t)DIT_NOALLOC_SCRATCH_BYTES)
+    return fail(DIT_ERR_UNSUPPORTED, "this call needs %zu bytes of workspace; the static scratch of "
+                "dit_attn_fwd_noalloc holds %zu (use dit_attn_fwd with a caller workspace)",
+                pl.total, (size_t)DIT_NOALLOC_SCRATCH_BYTES);
+  dit_attn_desc d = *desc;
+  d.workspace = nullptr;
+  d.workspace_bytes = 0;
+  d.ws_counters_zero = 0;   // the array keeps whatever the last call left: clear the counters
+  if (pl.total > 0) {
+    d.workspace = scratch_ptr(&rc);
+    if (rc != DIT_OK) return rc;
+    d.workspace_bytes = DIT_NOALLOC_SCRATCH_BYTES;
+  }
+  return dit_attn_fwd(&d, stream);
 }
 
 int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {

@@ -89,6 +89,9 @@ def test_attn_fwd_rejects_bad_arguments_before_any_hip_call(L, kw, code, msg):
     d = _desc(**kw)
     assert L.dit_attn_fwd(ctypes.byref(d), None) == code
     assert msg in L.dit_last_error()
+    # the allocation-free entry point validates the same way, before any HIP call
+    assert L.dit_attn_fwd_noalloc(ctypes.byref(d), None) == code
+    assert msg in L.dit_last_error()
 
 
 def test_attn_fwd_rejects_bad_strides_and_missing_workspace(L):
