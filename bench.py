@@ -11,6 +11,9 @@ valid tokens: FLOP = 4 * B * H * S_valid^2 * d per step.
 Prints ONE JSON line:
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-configs]
 
+Shader clock of the attention kernel's key loop per config (clock-probe build):
+  python bench.py --clock-probe
+
 Counter collection (HBM traffic of the attention kernel, calibrated against a
 plain copy of known size), run under rocprofv3 once per counter:
   python bench.py --pmc-target              # launches only the measured kernels
@@ -48,7 +51,10 @@ def parse():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config kernel table")
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--pmc-target", action="store_true")
+    ap.add_argument("--pmc-variant", default="percall", choices=("percall", "split", "seg", "fixed_m"))
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--clock-probe", action="store_true",
+                    help="shader clock of the attention kernel's key loop per config (clock-probe build)")
     ap.add_argument("--hbm-passes", action="store_true",
                     help="time the HBM-bound passes (pad, unpad, LSE merge, tables) on Wan 720p-sized buffers")
     return ap.parse_args()
@@ -290,8 +296,15 @@ def read_traffic():
 
 # ------------------------------------------------------- counter workflow
 def pmc_target(args):
-    """Launch the dominant kernel (attention without the rotation pre-pass)
-    and the calibration copy a few times each; nothing else runs on the GPU."""
+    """Launch one kernel variant a few times on its workload, plus the
+    calibration copy (for the traffic record); nothing else runs on the GPU.
+    --pmc-variant picks the variant:
+      percall  attn_fwd_kernel<128, false>, one workgroup per q-tile (the
+               step's kernel; Q and K unrotated, no pre-pass)
+      split    attn_fwd_kernel<128, true>, the split (BALANCED) schedule
+      seg      attn_fwd_seg_kernel<128>: the ring layout, two segments of
+               2340 real keys each padded to 2368 (Q likewise)
+      fixed_m  the fixed-m statistics kernels and the FIXED loop (forced)"""
     import numpy as np
     import torch
     import workloads as W
@@ -300,13 +313,26 @@ def pmc_target(args):
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     _, (qd, kd, vd) = dev_tensors(w, np, torch, dev)
+    kw = dict(q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=None, rope_k=None, fixed_m=False)
+    if args.pmc_variant == "split":
+        kw["schedule"] = 2
+    elif args.pmc_variant == "fixed_m":
+        kw["fixed_m"] = True
+    elif args.pmc_variant == "seg":
+        per, L = w.s_valid // 2, 2368
+        qs, ks, vs = (torch.zeros((w.B, w.H, 2 * L, w.d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+        for src, dst in ((qd, qs), (kd, ks), (vd, vs)):
+            for i in range(2):
+                dst[:, :, i * L:i * L + per] = src[:, :, i * per:(i + 1) * per]
+        qd, kd, vd = qs, ks, vs
+        kw.update(q_valid=per, kv_valid=per, q_seg_len=L, kv_seg_len=L)
+    elif args.pmc_variant != "percall":
+        raise SystemExit(f"unknown --pmc-variant {args.pmc_variant}")
     o = torch.empty_like(qd)
-    lse = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(256, ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid)),
-                     dtype=torch.uint8, device=dev)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, ops.attn_workspace_size(qd, kd, vd, **kw)), dtype=torch.uint8, device=dev)
     for i in range(5):   # the first call clears the schedule counters, the rest launch the attention kernel alone
-        ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=None, rope_k=None, out=o, lse=lse,
-                     workspace=ws, ws_counters_zero=i > 0)
+        ops.attn_fwd(qd, kd, vd, out=o, lse=lse, workspace=ws, ws_counters_zero=i > 0, **kw)
     src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
     src.fill_(1)
     dst = torch.empty_like(src)
@@ -364,6 +390,65 @@ def hbm_passes(args):
         res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / us / 1e3} if nbytes else {"us": us}
     res["prepass_algorithmic_bytes"] = prepass_bytes
     print(json.dumps({"hbm_passes_wan720": res}), flush=True)
+
+
+def clock_probe(args):
+    """Shader clock of the attention kernel's key loop, per config, from the
+    clock-probe build of the library (libditattn_clockprobe.so: the first
+    thread of each workgroup stamps the shader-clock counter and the 100 MHz
+    counter when its key loop starts and ends). The kernel alone runs on
+    each workload's Q, K, V for 1 s, then 3 rounds of 20 calls; the stamps
+    of each round's last call give, per workgroup, the loop's cycles and its
+    real time, hence the clock and the cycles per MFMA (each SIMD runs two
+    waves of 32 MFMAs per key tile). Prints one JSON line."""
+    import ctypes
+    import numpy as np
+    import torch
+    import workloads as W
+    from long_sequence_attention_amd import _native as N, build as Bld
+    N.LIB_PATH = Bld.LIB_CLOCK_PROBE
+    import long_sequence_attention_amd as ops
+    L = N.lib()
+    L.dit_clock_probe_read.argtypes = [ctypes.c_void_p]
+    L.dit_clock_probe_read.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"library": os.path.basename(Bld.LIB_CLOCK_PROBE), "compute_units": cus}
+    for name in ("wan480", "flux", "hunyuan", "wan720"):
+        w = W.WORKLOADS[name]
+        _, (qd, kd, vd) = dev_tensors(w, np, torch, dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev)
+        fn = lambda: ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, out=o, lse=lse, schedule=1,
+                                  fixed_m=False)
+        time_us(torch, fn, 1, warm_s=1.0)
+        nwg = w.B * w.H * (-(-w.s_pad // 256))
+        nk = -(-w.k_valid // 64)
+        buf = np.zeros(4096 * 4, dtype=np.uint64)
+        rounds = []
+        for _ in range(3):
+            for _ in range(20 if w.valid_flop < 1e12 else 2):
+                fn()
+            torch.cuda.synchronize()
+            if L.dit_clock_probe_read(buf.ctypes.data) != 0:
+                raise RuntimeError("dit_clock_probe_read failed")
+            b = buf[:min(nwg, 4096) * 4].reshape(-1, 4).astype(np.float64)
+            cyc, real = b[:, 2] - b[:, 0], b[:, 3] - b[:, 1]
+            mhz = cyc / real * 100.0
+            ent = {"workgroups": int(len(b)), "key_tiles": nk, "loop_us_median": float(np.median(real) / 100),
+                   "loop_cycles_median": float(np.median(cyc)), "mhz_median": float(np.median(mhz)),
+                   "mhz_min": float(mhz.min()), "mhz_max": float(mhz.max()),
+                   "cycles_per_mfma_median": float(np.median(cyc) / (nk * 64))}
+            if nwg > cus:   # workgroups of the first wave (every CU busy) against the rest
+                first = b[:, 1] < np.sort(b[:, 3])[0]
+                ent["mhz_median_first_wave"] = float(np.median(mhz[first]))
+                ent["mhz_median_later"] = float(np.median(mhz[~first])) if (~first).any() else None
+                ent["first_wave_workgroups"] = int(first.sum())
+            rounds.append(ent)
+        res[name] = rounds
+        del qd, kd, vd, o
+        torch.cuda.empty_cache()
+    print(json.dumps({"clock_probe": res}), flush=True)
 
 
 def traffic_summary(args):
@@ -444,14 +529,15 @@ def config_table(np, torch, ops, W, dev, n_iter, inputs=None):
             ent.update({"kernel_us": kus, "kernel_pct_peak": w.valid_flop / kus / 1e6 / PEAK_BF16_TFLOPS * 100,
                         "prepass_us": us - kus})
             del k_rot, q_rot
-        if name in ("wan480", "hunyuan", "wan720"):   # the fixed-m softmax (key / query statistics passes)
-            wsf = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
-                                                          rope_q=tabs, rope_k=tabs, fixed_m=True), 256),
-                              dtype=torch.uint8, device=dev)
-            ent["fixed_m_us"] = time_us(torch, lambda: ops.attn_fwd(
-                qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=tabs, rope_k=tabs, out=o, lse=lse,
-                workspace=wsf, fixed_m=True), n)
-            del wsf
+        if name in ("wan480", "hunyuan", "wan720"):   # the softmax forced each way (AUTO: fixed-m from 32768 keys)
+            for tag, fm in (("fixed_m_us", True), ("online_us", False)):
+                wsf = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
+                                                              rope_q=tabs, rope_k=tabs, fixed_m=fm), 256),
+                                  dtype=torch.uint8, device=dev)
+                ent[tag] = time_us(torch, lambda: ops.attn_fwd(
+                    qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=tabs, rope_k=tabs, out=o, lse=lse,
+                    workspace=wsf, fixed_m=fm), n)
+                del wsf
         if name == "wan480":   # the same call with the per-head q/k RMSNorm fused into the pre-pass
             wn = torch.ones(w.d, dtype=torch.float32, device=dev)
             wsn = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
@@ -524,6 +610,9 @@ def main():
         return
     if args.hbm_passes:
         hbm_passes(args)
+        return
+    if args.clock_probe:
+        clock_probe(args)
         return
     import ctypes
     import numpy as np

@@ -146,8 +146,11 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  * segment length (else DIT_ERR_INVALID); kv_seg_len must be a multiple of 64
  * (segmented calls run PER_QTILE whatever the schedule asks).
  *
- * fixed_m = 1 (the fixed-m softmax of maxdiffusion PR #491; the bound is not
- * printed there, the plain reading is used): before the attention kernel,
+ * fixed_m selects the fixed-m softmax (maxdiffusion PR #491; the bound is
+ * not printed there, the plain reading is used): 1 = on, 2 = off (online
+ * softmax), 0 = AUTO: on where a head has at least 32768 real keys (then its
+ * statistics passes cost a small part of the call and the loop without a
+ * running maximum wins, e.g. the Wan 720p shard), off below. When on: before the attention kernel,
  * passes over K (and Q) compute, over the real keys of each head, the key
  * mean kbar and R = max_j |k_j - kbar|, and for every query row the bound
  *   m_i = sm_scale * (q_i . kbar + |q_i| R) >= every score of row i
@@ -176,13 +179,13 @@ typedef struct dit_attn_desc {
   const float *q_norm_w, *k_norm_w;  /* fp32 [d] RMSNorm weights or NULL (no norm) */
   float norm_eps;
   int32_t q_seg_len, kv_seg_len; /* 0, or segment length: see "Segments" above */
-  int32_t fixed_m;               /* 0 = online softmax, 1 = fixed-m: see above */
+  int32_t fixed_m;               /* 0 = AUTO, 1 = fixed-m, 2 = online softmax: see above */
   int32_t ws_counters_zero;      /* 1: the workspace's Stream-K counters are known zero; see above */
 } dit_attn_desc;
 
 /* Bytes of workspace dit_attn_fwd needs for `desc` (0 when neither Q nor K
  * is rotated or normalised, the schedule needs no partial results and
- * fixed_m is 0, or when kv_valid is 0). Under BALANCED and AUTO the schedule
+ * the fixed-m softmax is off, or when kv_valid is 0). Under BALANCED and AUTO the schedule
  * and the size depend on the current device's compute-unit count
  * (DIT_ERR_HIP if it cannot be queried). */
 DIT_API int dit_attn_workspace_size(const dit_attn_desc *desc, size_t *bytes);

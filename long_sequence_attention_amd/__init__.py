@@ -70,7 +70,7 @@ def plan_padding(s_valid: int, multiple: int) -> int:
 
 
 def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule=0,
-               q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False,
+               q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=None,
                ws_counters_zero=False):
     B, H, s_q, d = q.shape
     desc = N.AttnDesc()
@@ -94,13 +94,13 @@ def _attn_desc(q, k, v, o, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, sch
         desc.k_norm_w = k_norm.data_ptr()
     desc.norm_eps = float(norm_eps)
     desc.q_seg_len, desc.kv_seg_len = int(q_seg_len), int(kv_seg_len)
-    desc.fixed_m = 1 if fixed_m else 0
+    desc.fixed_m = 0 if fixed_m is None else (1 if fixed_m else 2)
     desc.ws_counters_zero = 1 if ws_counters_zero else 0
     return desc
 
 
 def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, schedule=0,
-                        q_norm=None, k_norm=None, q_seg_len=0, kv_seg_len=0, fixed_m=False) -> int:
+                        q_norm=None, k_norm=None, q_seg_len=0, kv_seg_len=0, fixed_m=None) -> int:
     """Workspace bytes attn_fwd needs (dit_attn_workspace_size) on q's device."""
     q_valid = (q_seg_len or q.shape[2]) if q_valid is None else int(q_valid)
     kv_valid = (kv_seg_len or k.shape[2]) if kv_valid is None else int(kv_valid)
@@ -114,7 +114,7 @@ def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, ro
 
 def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
              out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, workspace=None, schedule=0,
-             q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False,
+             q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=None,
              ws_counters_zero=False, _noalloc=False):
     """Attention forward (dit_attn_fwd).
 
@@ -126,8 +126,10 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
     q_norm / k_norm: fp32 [d] RMSNorm weights (per-head q/k RMS normalisation
     before RoPE, epsilon norm_eps) or None. q_seg_len / kv_seg_len > 0: the
     rows form segments of that length, each padded at its own tail, and
-    q_valid / kv_valid count the real rows of each segment. fixed_m: use the
-    a-priori row-max bound where it is tight enough (dit_attn_desc.fixed_m).
+    q_valid / kv_valid count the real rows of each segment. fixed_m: True =
+    the fixed-m softmax (a-priori row-max bound where it is tight enough),
+    False = the online softmax, None = AUTO (fixed-m for at least 32768 real
+    keys per head; dit_attn_desc.fixed_m).
     ws_counters_zero: the caller's `workspace` comes unchanged from an earlier
     completed call with the same arguments, so its schedule counters are
     already zero and the call skips clearing them.
@@ -195,7 +197,7 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
 
 def attn_fwd_noalloc(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, sm_scale=0.0,
                      out=None, out_dtype=torch.bfloat16, lse=None, return_lse=True, schedule=0,
-                     q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=False):
+                     q_norm=None, k_norm=None, norm_eps=1e-6, q_seg_len=0, kv_seg_len=0, fixed_m=None):
     """dit_attn_fwd_noalloc: attn_fwd with the library's static device scratch
     (NOALLOC_SCRATCH_BYTES per GPU) as the workspace; the library allocates
     nothing (pass `out` and `lse` to allocate nothing here either). Calls on

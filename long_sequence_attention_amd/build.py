@@ -20,6 +20,9 @@ LIB = os.path.join(LIBDIR, "libditattn.so")
 # the same sources with a wait and a barrier after every DMA issue and LDS
 # read phase of the attention kernel (results must equal LIB's bit for bit)
 LIB_DEBUG_SYNC = os.path.join(LIBDIR, "libditattn_debugsync.so")
+# the same sources with shader-clock stamps around each workgroup's key loop
+# (bench.py --clock-probe reads them)
+LIB_CLOCK_PROBE = os.path.join(LIBDIR, "libditattn_clockprobe.so")
 SOURCES = ["api.hip", "attn_fwd.hip", "elementwise.hip", "fixed_m.hip"]
 
 HIPCC_FLAGS = [
@@ -61,7 +64,7 @@ def is_current() -> bool:
             recorded = f.read().strip()
     except OSError:
         return False
-    return os.path.exists(LIB) and os.path.exists(LIB_DEBUG_SYNC) and recorded == source_hash()
+    return all(os.path.exists(x) for x in (LIB, LIB_DEBUG_SYNC, LIB_CLOCK_PROBE)) and recorded == source_hash()
 
 
 def hipcc() -> str:
@@ -77,12 +80,14 @@ def _command(out, extra_flags):
 
 
 def build(verbose: bool = False, extra_flags=None, debug_sync: bool = True) -> str:
-    """Compile LIB (and, unless debug_sync is False, LIB_DEBUG_SYNC alongside
-    it in a second compiler process); returns LIB's path."""
+    """Compile LIB (and, unless debug_sync is False, LIB_DEBUG_SYNC and
+    LIB_CLOCK_PROBE alongside it in parallel compiler processes); returns
+    LIB's path."""
     os.makedirs(LIBDIR, exist_ok=True)
     jobs = [(LIB, list(extra_flags or []))]
     if debug_sync:
         jobs.append((LIB_DEBUG_SYNC, list(extra_flags or []) + ["-DDIT_DEBUG_SYNC=1"]))
+        jobs.append((LIB_CLOCK_PROBE, list(extra_flags or []) + ["-DDIT_CLOCK_PROBE=1"]))
     procs = []
     for out, flags in jobs:
         cmd = _command(out + ".tmp", flags)

@@ -84,7 +84,7 @@ int validate_attn(const dit_attn_desc *d, float *scale_out) {
   if (d->kv_seg_len > 0 && d->kv_seg_len % dit::kAttnBlockN != 0)
     return fail(DIT_ERR_UNSUPPORTED, "kv_seg_len=%d must be a multiple of the %d-row key tile", d->kv_seg_len,
                 dit::kAttnBlockN);
-  if (d->fixed_m != 0 && d->fixed_m != 1) return fail(DIT_ERR_INVALID, "fixed_m=%d must be 0 or 1", d->fixed_m);
+  if (d->fixed_m < 0 || d->fixed_m > 2) return fail(DIT_ERR_INVALID, "fixed_m=%d must be 0, 1 or 2", d->fixed_m);
   if (d->ws_counters_zero != 0 && d->ws_counters_zero != 1)
     return fail(DIT_ERR_INVALID, "ws_counters_zero=%d must be 0 or 1", d->ws_counters_zero);
   if (d->o_dtype != DIT_BF16 && d->o_dtype != DIT_F32) return fail(DIT_ERR_INVALID, "o_dtype=%d is not a dit_dtype", d->o_dtype);
@@ -198,8 +198,22 @@ int device_cus() {
   if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
+// fixed_m = 0 (AUTO) takes the fixed-m softmax where a head has at least
+// kFixedMMinKeys real keys: its statistics passes (a few us) are then a
+// small part of the call and the loop without a running maximum wins (Wan
+// 720p, 75,600 keys: 23,984 against 24,311 us); on shorter key ranges the
+// passes cost more than they save (Wan 480p: 139.7 against 118.2 us).
+constexpr int64_t kFixedMMinKeys = 32768;
+bool use_fixed_m(const dit_attn_desc *d) {
+  if (d->fixed_m == 1) return true;
+  if (d->fixed_m == 2) return false;
+  const int64_t real_keys = d->kv_seg_len > 0 ? (int64_t)(d->s_kv / d->kv_seg_len) * d->kv_valid : d->kv_valid;
+  return real_keys >= kFixedMMinKeys;
+}
+
 int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   AttnPlan p;
+  const bool fm = use_fixed_m(d);
   if ((d->cos_k != nullptr || d->k_norm_w != nullptr) && d->kv_valid > 0)
     p.k_bytes = round_up((size_t)d->B * d->H * (size_t)d->s_kv * d->d * 2, 256);
   if ((d->cos_q != nullptr || d->q_norm_w != nullptr) && d->kv_valid > 0)
@@ -210,7 +224,7 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
     return fail(DIT_ERR_INVALID, "schedule=%d is not a dit_schedule", d->schedule);
   // the split schedule covers plain (one-segment, online-softmax) calls with
   // at least two key tiles when BALANCED asks for it (see split_pays for AUTO)
-  if (d->schedule != DIT_SCHED_PER_QTILE && nq > 0 && nk >= 2 && d->kv_seg_len == 0 && !d->fixed_m) {
+  if (d->schedule != DIT_SCHED_PER_QTILE && nq > 0 && nk >= 2 && d->kv_seg_len == 0 && !fm) {
     const int cus = device_cus();
     if (cus <= 0 && d->schedule == DIT_SCHED_BALANCED)
       return fail(DIT_ERR_HIP, "cannot query the compute-unit count of the current device");
@@ -232,7 +246,7 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
     p.n_counts = nq;
     off += round_up((size_t)nq * sizeof(int32_t), 256);
   }
-  if (d->fixed_m && d->kv_valid > 0 && d->s_q > 0) {
+  if (fm && d->kv_valid > 0 && d->s_q > 0) {
     const size_t bh = (size_t)d->B * d->H;
     const int64_t nqt = (d->s_q + kBlockM - 1) / kBlockM;
     p.fm = true;

@@ -80,6 +80,30 @@ __device__ __forceinline__ u32x4 ldg16(const bf16_t *p) { return *reinterpret_ca
 #ifndef DIT_DEBUG_SYNC
 #define DIT_DEBUG_SYNC 0
 #endif
+// Clock probe build (compiled with -DDIT_CLOCK_PROBE=1 into a separate
+// library): the first thread of each of the first kClockProbeWgs workgroups
+// of the one-workgroup-per-q-tile kernel records the shader-clock counter
+// (s_memtime) and the constant 100 MHz counter (s_memrealtime) when its key
+// loop starts and when it ends; their ratio is the shader clock the loop ran
+// at. The arithmetic is unchanged.
+#ifndef DIT_CLOCK_PROBE
+#define DIT_CLOCK_PROBE 0
+#endif
+constexpr int kClockProbeWgs = 4096;
+#if DIT_CLOCK_PROBE
+__device__ unsigned long long g_clock_probe[kClockProbeWgs * 4];
+#endif
+__device__ __forceinline__ void clock_mark(int k) {
+#if DIT_CLOCK_PROBE
+  if (threadIdx.x == 0 && blockIdx.x < kClockProbeWgs) {
+    g_clock_probe[blockIdx.x * 4 + 2 * k] = __builtin_amdgcn_s_memtime();
+    g_clock_probe[blockIdx.x * 4 + 2 * k + 1] = __builtin_amdgcn_s_memrealtime();
+  }
+#else
+  (void)k;
+#endif
+}
+
 __device__ __forceinline__ void debug_sync() {
   if constexpr (DIT_DEBUG_SYNC != 0) {
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
@@ -457,6 +481,7 @@ __device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &
     }
   }
 
+  if (FIRST) clock_mark(0);
   StepCtx<D> cx{smem, wbase, kbase, vbase, ln.koff, ln.voff, ln.kx, ln.vx, qop,
                 ln.ks_bytes, ln.vs_bytes, kv_end, ke, ln.wave, ln.hf, c2};
   // steady state: tiles t, t+1, t+2 all full; two tiles per iteration so the
@@ -794,6 +819,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
     }
+    clock_mark(1);
     const float l_tot = pair_sum(l_run);
     const bool row_ok = query_is_real(p, qrow) && (nk > 0);
     store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
@@ -1059,3 +1085,13 @@ hipError_t launch_rope_rotate(const RopeRotateParams &p, hipStream_t stream) {
 int attn_block_m() { return BM; }
 
 }  // namespace dit
+
+#if DIT_CLOCK_PROBE
+// Probe build only: copy the stamps of the last launch (4 words per
+// workgroup: shader clock and 100 MHz counter at loop start, then at loop
+// end) to host memory; returns a hipError_t.
+extern "C" __attribute__((visibility("default"))) int dit_clock_probe_read(unsigned long long *host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(dit::g_clock_probe), sizeof(dit::g_clock_probe), 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif

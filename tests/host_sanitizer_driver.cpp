@@ -58,7 +58,7 @@ int main() {
     {"segments < 0", [](dit_attn_desc &d) { d.kv_seg_len = -1; }, DIT_ERR_INVALID, "segment lengths"},
     {"s_kv % kv_seg_len", [](dit_attn_desc &d) { d.kv_seg_len = 100; }, DIT_ERR_INVALID, "multiple of kv_seg_len"},
     {"kv_seg_len not tile", [](dit_attn_desc &d) { d.kv_seg_len = 32; d.kv_valid = 32; }, DIT_ERR_UNSUPPORTED, "key tile"},
-    {"fixed_m = 2", [](dit_attn_desc &d) { d.fixed_m = 2; }, DIT_ERR_INVALID, "fixed_m"},
+    {"fixed_m = 3", [](dit_attn_desc &d) { d.fixed_m = 3; }, DIT_ERR_INVALID, "fixed_m"},
     {"ws_counters_zero", [](dit_attn_desc &d) { d.ws_counters_zero = 3; }, DIT_ERR_INVALID, "ws_counters_zero"},
     {"schedule", [](dit_attn_desc &d) { d.schedule = 9; }, DIT_ERR_INVALID, "schedule"},
     {"misaligned q", [](dit_attn_desc &d) { d.q = reinterpret_cast<void *>(uintptr_t(0x10000008)); }, DIT_ERR_UNSUPPORTED, "16-byte aligned"},

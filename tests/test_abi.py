@@ -82,7 +82,7 @@ def _desc(**kw):
     (dict(q_seg_len=128, q_valid=200), -1, b"q_valid"),
     (dict(kv_seg_len=32, kv_valid=32), -2, b"key tile"),
     (dict(kv_seg_len=-1), -1, b"segment lengths"),
-    (dict(fixed_m=2), -1, b"fixed_m"),
+    (dict(fixed_m=3), -1, b"fixed_m"),
     (dict(ws_counters_zero=3), -1, b"ws_counters_zero"),
 ])
 def test_attn_fwd_rejects_bad_arguments_before_any_hip_call(L, kw, code, msg):

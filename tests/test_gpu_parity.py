@@ -381,7 +381,7 @@ def test_fixed_m_with_shifted_keys_segments_and_pads(ops):
 
 def test_fixed_m_falls_back_to_online_for_a_loose_bound(ops):
     """Q x 8: the bound's spread exceeds the fixed-m limit on every q-tile, so
-    every q-tile keeps the online softmax: the same bits as fixed_m = 0."""
+    every q-tile keeps the online softmax: the same bits as the online path."""
     import torch
     say("fixed-m fallback (Q x 8)")
     r = np.random.default_rng(55)
@@ -633,8 +633,13 @@ def test_wan720_single_pass_and_four_shard_merge(ops):
     cos, sin = tabs
     q, k, v = W.make_qkv(w)
     qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
-    o1, l1 = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs)
+    o1, l1 = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs, fixed_m=False)
     o3, l3 = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs, fixed_m=True)
+    # AUTO (the default) takes the fixed-m softmax at 75,600 real keys: the same bits as forcing it
+    o4, l4 = ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs)
+    torch.cuda.synchronize()
+    assert torch.equal(o4.view(torch.int16), o3.view(torch.int16)) and torch.equal(l4, l3)
+    del o4, l4
     parts_o, parts_l = [], []
     for (s0, L, kvv) in W.key_shards(w):
         po, pl = ops.attn_fwd(qd, kd[:, :, s0:s0 + L], vd[:, :, s0:s0 + L], q_valid=w.s_valid, kv_valid=kvv,
