@@ -7,6 +7,7 @@ prefix.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 
@@ -24,6 +25,14 @@ NOALLOC_SCRATCH_BYTES = 128 << 20   # DIT_NOALLOC_SCRATCH_BYTES
 def library_path() -> str:
     N.lib()
     return N.LIB_PATH
+
+
+def _on_device(dev: torch.device):
+    """Make dev current for the library call (it launches on the current
+    device); a no-op when it already is."""
+    if dev.index is None or torch.cuda.current_device() == dev.index:
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
 
 
 def _stream(dev: torch.device) -> ctypes.c_void_p:
@@ -107,7 +116,7 @@ def attn_workspace_size(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, ro
     desc = _attn_desc(q, k, v, q, None, q_valid, kv_valid, rope_q, rope_k, 0.0, schedule, q_norm, k_norm,
                       q_seg_len=q_seg_len, kv_seg_len=kv_seg_len, fixed_m=fixed_m)
     need = ctypes.c_size_t()
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_workspace_size")
     return need.value
 
@@ -173,24 +182,21 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
         raise ValueError("ws_counters_zero needs the caller's workspace")
     desc = _attn_desc(q, k, v, out, lse, q_valid, kv_valid, rope_q, rope_k, sm_scale, schedule, q_norm, k_norm,
                       norm_eps, q_seg_len, kv_seg_len, fixed_m, ws_counters_zero)
-    if _noalloc:
-        with torch.cuda.device(q.device):
+    with _on_device(q.device):
+        if _noalloc:
             N.check(N.lib().dit_attn_fwd_noalloc(ctypes.byref(desc), _stream(q.device)), "attn_fwd_noalloc")
-        return (out, lse) if return_lse else out
-    need = ctypes.c_size_t()
-    with torch.cuda.device(q.device):
-        N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")
-    if need.value:
-        if workspace is None:
-            workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-        _need_cuda("workspace", workspace)
-        if not workspace.is_contiguous():
-            raise ValueError("workspace must be a dense tensor")
-        if workspace.numel() * workspace.element_size() < need.value:
-            raise ValueError(f"workspace needs {need.value} bytes")
-        desc.workspace = workspace.data_ptr()
-        desc.workspace_bytes = workspace.numel() * workspace.element_size()
-    with torch.cuda.device(q.device):
+            return (out, lse) if return_lse else out
+        if workspace is None:   # ask the library how much it needs and allocate that
+            need = ctypes.c_size_t()
+            N.check(N.lib().dit_attn_workspace_size(ctypes.byref(desc), ctypes.byref(need)), "attn_fwd")
+            if need.value:
+                workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        if workspace is not None:   # the library checks its size against the call
+            _need_cuda("workspace", workspace)
+            if not workspace.is_contiguous():
+                raise ValueError("workspace must be a dense tensor")
+            desc.workspace = workspace.data_ptr()
+            desc.workspace_bytes = workspace.numel() * workspace.element_size()
         N.check(N.lib().dit_attn_fwd(ctypes.byref(desc), _stream(q.device)), "attn_fwd")
     return (out, lse) if return_lse else out
 
@@ -241,10 +247,11 @@ def lse_merge(o_parts, lse_parts, *, q_valid=None, out_dtype=torch.bfloat16, out
         _check_out("lse_out", lse_out, (B, H, S), (torch.float32,), dev)
     optr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in o_parts])
     lptr = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
-    rc = N.lib().dit_lse_merge(n, optr, lptr, N.DIT_F32 if pdt == torch.float32 else N.DIT_BF16,
-                               B, H, S, d, q_valid, _ptr(out),
-                               N.DIT_F32 if out.dtype == torch.float32 else N.DIT_BF16,
-                               _ptr(lse_out), _stream(dev))
+    with _on_device(dev):
+        rc = N.lib().dit_lse_merge(n, optr, lptr, N.DIT_F32 if pdt == torch.float32 else N.DIT_BF16,
+                                   B, H, S, d, q_valid, _ptr(out),
+                                   N.DIT_F32 if out.dtype == torch.float32 else N.DIT_BF16,
+                                   _ptr(lse_out), _stream(dev))
     N.check(rc, "lse_merge")
     return (out, lse_out) if return_lse else out
 
@@ -261,8 +268,9 @@ def rope_split_tables(pos, axis_channels, d: int, theta: float = 10000.0):
         raise ValueError("one channel count per position column")
     cos = torch.empty((S, d // 2), dtype=torch.float32, device=pos.device)
     sin = torch.empty_like(cos)
-    N.check(N.lib().dit_rope_split_tables(_ptr(pos), S, n_axes, chans, int(d), float(theta), _ptr(cos),
-                                          _ptr(sin), _stream(pos.device)), "rope_split_tables")
+    with _on_device(pos.device):
+        N.check(N.lib().dit_rope_split_tables(_ptr(pos), S, n_axes, chans, int(d), float(theta), _ptr(cos),
+                                              _ptr(sin), _stream(pos.device)), "rope_split_tables")
     return cos, sin
 
 
@@ -277,8 +285,9 @@ def pad_tokens(x, s_pad: int, out=None):
         out = torch.empty((B, s_pad) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
     else:
         _check_out("out", out, (B, int(s_pad)) + tuple(x.shape[2:]), (x.dtype,), x.device)
-    N.check(N.lib().dit_pad_tokens(_ptr(x), _ptr(out), B, s_valid, int(s_pad), row_bytes, _stream(x.device)),
-            "pad_tokens")
+    with _on_device(x.device):
+        N.check(N.lib().dit_pad_tokens(_ptr(x), _ptr(out), B, s_valid, int(s_pad), row_bytes, _stream(x.device)),
+                "pad_tokens")
     return out
 
 
@@ -293,6 +302,7 @@ def unpad_tokens(x, s_valid: int, out=None):
         out = torch.empty((B, int(s_valid)) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
     else:
         _check_out("out", out, (B, int(s_valid)) + tuple(x.shape[2:]), (x.dtype,), x.device)
-    N.check(N.lib().dit_unpad_tokens(_ptr(x), _ptr(out), B, s_pad, int(s_valid), row_bytes, _stream(x.device)),
-            "unpad_tokens")
+    with _on_device(x.device):
+        N.check(N.lib().dit_unpad_tokens(_ptr(x), _ptr(out), B, s_pad, int(s_valid), row_bytes, _stream(x.device)),
+                "unpad_tokens")
     return out

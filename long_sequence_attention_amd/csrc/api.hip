@@ -147,31 +147,50 @@ struct AttnPlan {
 constexpr int kBlockM = dit::kAttnBlockM, kBlockN = dit::kAttnBlockN, kThreads = dit::kAttnThreads;
 
 // Split schedule for nq q-tiles of nk key tiles on `cus` compute units
-// (one workgroup per CU). When the q-tiles fill less than one wave
-// (nq < cus): nq main workgroups run keys [0, kc) of their q-tile in step
-// and the cus - nq spare CUs split the remaining key tails evenly; kc is
-// chosen so that a main workgroup's kc tiles match a helper's share of the
-// tails plus kPieceCost tile-steps for the helper's extra Q loads and
-// partial stores. Otherwise (or when that leaves no tail) plain Stream-K
-// over all units.
-constexpr int64_t kPieceCost = 4;
+// (one workgroup per CU). Two shapes, modelled in tile-steps, the cheaper
+// one taken. A workgroup whose run of units touches a q-tile it does not
+// finish pays kPieceCost tile-steps for that piece (its Q load and partial
+// store); a run of u units over q-tiles of t units touches at most
+// ceil(u / t) + 1 of them, and a q-tile of t units split into runs of u is
+// in at most ceil(t / u) + 1 pieces, which its last piece merges at
+// kMergeCost tile-steps each.
+//  - hybrid (nq < cus): nq main workgroups run keys [0, kc) of their q-tile
+//    and up to cus - nq helpers split the nq * (nk - kc) tail units into
+//    equal contiguous runs; the tail length is the one that minimises the
+//    larger of kc and the busiest helper's units plus piece costs, plus the
+//    merge;
+//  - plain Stream-K: min(nq * nk, cus) workgroups split all units evenly.
+constexpr int64_t kPieceCost = 4, kMergeCost = 1;
 struct SplitPlan {
   int grid = 0, main = 0, kc = 0;
 };
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 SplitPlan split_plan(int64_t nq, int64_t nk, int64_t cus) {
   SplitPlan sp;
-  if (nq < cus && nk >= 2) {
-    int64_t helpers = cus - nq;
-    int64_t kc = (nq * nk + helpers * kPieceCost + cus - 1) / cus;
-    kc = kc < 1 ? 1 : (kc > nk - 1 ? nk - 1 : kc);
-    const int64_t tail_units = nq * (nk - kc);
-    if (helpers > tail_units) helpers = tail_units;
-    sp.grid = (int)(nq + helpers);
-    sp.main = (int)nq;
-    sp.kc = (int)kc;
-  } else {
-    const int64_t units = nq * nk;
-    sp.grid = (int)(units < cus ? units : cus);
+  const int64_t units = nq * nk;
+  const int64_t grid = units < cus ? units : cus;
+  const int64_t per_sk = ceil_div(units, grid);
+  int64_t best = per_sk + (ceil_div(per_sk, nk) + 1) * kPieceCost + (ceil_div(nk, per_sk) + 1) * kMergeCost;
+  sp.grid = (int)grid;
+  if (nq < cus) {
+    int64_t hb = -1, ht = 0, hh = 0;   // the best hybrid: cost, tail length, helpers
+    for (int64_t t = 1; t < nk; ++t) {
+      const int64_t tail = nq * t;
+      const int64_t h = cus - nq < tail ? cus - nq : tail;
+      const int64_t per = ceil_div(tail, h);   // the busiest helper's units
+      const int64_t helper = per + (ceil_div(per, t) + 1) * kPieceCost;
+      const int64_t cost = (nk - t > helper ? nk - t : helper) + (ceil_div(t, per) + 2) * kMergeCost;
+      if (hb < 0 || cost < hb) {   // ties keep the shorter tail (fewer pieces)
+        hb = cost;
+        ht = t;
+        hh = h;
+      }
+    }
+    if (hb >= 0 && hb <= best) {   // ties go to the hybrid (fewer pieces per q-tile)
+      sp.grid = (int)(nq + hh);
+      sp.main = (int)nq;
+      sp.kc = (int)(nk - ht);
+    }
   }
   return sp;
 }

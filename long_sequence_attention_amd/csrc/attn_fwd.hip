@@ -89,8 +89,8 @@ __device__ __forceinline__ u32x4 ldg16(const bf16_t *p) { return *reinterpret_ca
 #ifndef DIT_CLOCK_PROBE
 #define DIT_CLOCK_PROBE 0
 #endif
-constexpr int kClockProbeWgs = 4096;
 #if DIT_CLOCK_PROBE
+constexpr int kClockProbeWgs = 4096;
 __device__ unsigned long long g_clock_probe[kClockProbeWgs * 4];
 #endif
 __device__ __forceinline__ void clock_mark(int k) {
@@ -393,6 +393,26 @@ __device__ __forceinline__ void load_q(const P &p, const Lane<D> &ln, int b, int
   for (int dk = 0; dk < DK; ++dk) qop[dk] = __builtin_bit_cast(bf16x8, raw[dk]);
 }
 
+// Whether query row qrow is a real token: q_valid counts the real rows of
+// the whole sequence, or of each q_seg_len-row segment when q_seg_len > 0.
+template <class P>
+__device__ __forceinline__ bool query_is_real(const P &p, int qrow) {
+  return p.q_seg_len > 0 ? (qrow < p.s_q && qrow % p.q_seg_len < p.q_valid) : qrow < p.q_valid;
+}
+
+// Whether any of the 32 rows r0 .. r0 + 31 of a wave is real, from
+// wave-uniform values only (so the branch on it stays uniform). With
+// segments: either r0 itself is real, or the first row of the next segment
+// lies in the range (it is real whenever q_valid > 0).
+template <class P>
+__device__ __forceinline__ bool wave_has_real_row(const P &p, int r0) {
+  if (p.q_seg_len == 0) return r0 < p.q_valid;
+  const int end = r0 + 32 < p.s_q ? r0 + 32 : p.s_q;
+  if (r0 >= end || p.q_valid == 0) return false;
+  const int off = r0 % p.q_seg_len;
+  return off < p.q_valid || r0 - off + p.q_seg_len < end;
+}
+
 // Attention of one q-tile (BM rows of head (b, h)) over the key tiles
 // [kb, ke), whose rows at or past kv_end are pads (they are fetched as zeros
 // and masked). FIRST: the first key range of the q-tile: Q is loaded into
@@ -418,10 +438,11 @@ __device__ __forceinline__ void run_keys(const P &p, char *smem, const Lane<D> &
   if (kb + 1 < ke) issue_rows<D, G::K0 + G::TILE_BYTES>(wbase, kbase, ln.ks_bytes, kb + 1, kv_end, ln.koff);
   debug_sync();
 
-  // a wave whose 32 query rows are all tail pads (rows >= q_valid) does
-  // no arithmetic: it still issues its share of every K/V tile and meets
-  // the others at each barrier, and its rows are written as pads
-  if (p.q_seg_len == 0 && qt * BM + ln.wave * 32 >= p.q_valid) {
+  // a wave whose 32 query rows are all pads (tail pads of the sequence or
+  // of their segments, or rows past s_q) does no arithmetic: it still
+  // issues its share of every K/V tile and meets the others at each
+  // barrier, and its rows are written as pads
+  if (!wave_has_real_row(p, qt * BM + ln.wave * 32)) {
     if (FIRST) {
       l_run = 0.f;
       m_run = 0.f;
@@ -514,13 +535,6 @@ __device__ __forceinline__ void run_qtile(const P &p, char *smem, const Lane<D> 
 template <class P>
 __device__ __forceinline__ bool use_fixed_m(const P &p, int b, int h, int qt) {
   return p.fm_m != nullptr && p.fm_ok[((int64_t)b * p.H + h) * p.n_qtiles + qt] != 0;
-}
-
-// Whether query row qrow is a real token: q_valid counts the real rows of
-// the whole sequence, or of each q_seg_len-row segment when q_seg_len > 0.
-template <class P>
-__device__ __forceinline__ bool query_is_real(const P &p, int qrow) {
-  return p.q_seg_len > 0 ? (qrow < p.s_q && qrow % p.q_seg_len < p.q_valid) : qrow < p.q_valid;
 }
 
 __device__ __forceinline__ float pair_sum(float x) {

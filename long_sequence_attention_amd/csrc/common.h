@@ -73,8 +73,8 @@ struct AttnParams {
   // remaining key tails Stream-K style (sk_main = sk_kc = 0: plain Stream-K
   // over every unit); the pieces of a q-tile meet in the workspace below
   int32_t sk_grid, sk_main, sk_kc;
-  float *sk_part_o;  // [sk_main + 2 helpers][kAttnThreads][d/2] partial O / l, fp32
-  float *sk_part_l;  // [sk_main + 2 helpers][kAttnBlockM rows] partial LSE, log2 units
+  float *sk_part_o;  // [2 sk_grid slots][kAttnThreads][d/2] partial O / l, fp32
+  float *sk_part_l;  // [2 sk_grid slots][kAttnBlockM rows] partial LSE, log2 units
   int32_t *sk_count; // [q-tiles] arrival counters, zero on entry (left zero on exit)
   // fixed-m softmax (fm_m != nullptr): row bounds [B*H][s_q] and per-q-tile
   // flags [B*H][n_qtiles] from launch_fixed_m
