@@ -528,6 +528,13 @@ def clock_probe(args):
                    "loop_cycles_median": float(np.median(cyc)), "mhz_median": float(np.median(mhz)),
                    "mhz_min": float(mhz.min()), "mhz_max": float(mhz.max()),
                    "cycles_per_mfma_median": float(np.median(cyc) / (nk * 64))}
+            # workgroup i runs on XCD i % 8 (round-robin dispatch): per-XCD
+            # medians of the clock and of the loop's cycles and time
+            xcd = np.arange(len(b)) % 8
+            ent["per_xcd"] = [{"workgroups": int((xcd == x).sum()), "mhz": float(np.median(mhz[xcd == x])),
+                               "loop_cycles": float(np.median(cyc[xcd == x])),
+                               "loop_us": float(np.median(real[xcd == x]) / 100),
+                               "loop_us_max": float(real[xcd == x].max() / 100)} for x in range(8) if (xcd == x).any()]
             if nwg > cus:   # workgroups of the first wave (every CU busy) against the rest
                 first = b[:, 1] < np.sort(b[:, 3])[0]
                 ent["mhz_median_first_wave"] = float(np.median(mhz[first]))
