@@ -513,21 +513,29 @@ def clock_probe(args):
         time_us(torch, fn, 1, warm_s=1.0)
         nwg = w.B * w.H * (-(-w.s_pad // 256))
         nk = -(-w.k_valid // 64)
-        buf = np.zeros(4096 * 4, dtype=np.uint64)
+        buf = np.zeros(4096 * 8, dtype=np.uint64)
         rounds = []
         for _ in range(3):
-            for _ in range(20 if w.valid_flop < 1e12 else 2):
-                fn()
-            torch.cuda.synchronize()
+            n_calls = 20 if w.valid_flop < 1e12 else 2
+            call_us = time_us(torch, fn, n_calls, warm=0)   # the round's calls, back to back
             if L.dit_clock_probe_read(buf.ctypes.data) != 0:
                 raise RuntimeError("dit_clock_probe_read failed")
-            b = buf[:min(nwg, 4096) * 4].reshape(-1, 4).astype(np.float64)
+            b = buf[:min(nwg, 4096) * 8].reshape(-1, 8).astype(np.float64)
             cyc, real = b[:, 2] - b[:, 0], b[:, 3] - b[:, 1]
             mhz = cyc / real * 100.0
             ent = {"workgroups": int(len(b)), "key_tiles": nk, "loop_us_median": float(np.median(real) / 100),
                    "loop_cycles_median": float(np.median(cyc)), "mhz_median": float(np.median(mhz)),
                    "mhz_min": float(mhz.min()), "mhz_max": float(mhz.max()),
                    "cycles_per_mfma_median": float(np.median(cyc) / (nk * 64))}
+            # the last call's launch: workgroup entry (word 4) to loop start,
+            # loop end to stores complete (word 5), and the span from the
+            # first entry to the last exit against the per-call time
+            entry, exit_ = b[:, 4], b[:, 5]
+            ent.update({"call_us": call_us, "span_us": float((exit_.max() - entry.min()) / 100),
+                        "entry_spread_us": float((entry.max() - entry.min()) / 100),
+                        "prologue_us_median": float(np.median(b[:, 1] - entry) / 100),
+                        "epilogue_us_median": float(np.median(exit_ - b[:, 3]) / 100)})
+            ent["outside_workgroups_us"] = call_us - ent["span_us"]
             # workgroup i runs on XCD i % 8 (round-robin dispatch): per-XCD
             # medians of the clock and of the loop's cycles and time
             xcd = np.arange(len(b)) % 8

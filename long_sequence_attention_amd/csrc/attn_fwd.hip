@@ -84,21 +84,37 @@ __device__ __forceinline__ u32x4 ldg16(const bf16_t *p) { return *reinterpret_ca
 // library): the first thread of each of the first kClockProbeWgs workgroups
 // of the one-workgroup-per-q-tile kernel records the shader-clock counter
 // (s_memtime) and the constant 100 MHz counter (s_memrealtime) when its key
-// loop starts and when it ends; their ratio is the shader clock the loop ran
-// at. The arithmetic is unchanged.
+// loop starts and when it ends (words 0-3 of its 8), and the 100 MHz
+// counter when the workgroup starts (word 4) and once every wave's O / LSE
+// stores have completed (word 5). Clock = loop cycles / loop time; the
+// entry and exit stamps place the prologue, the epilogue and the time
+// outside the workgroups in the launch. The arithmetic is unchanged.
 #ifndef DIT_CLOCK_PROBE
 #define DIT_CLOCK_PROBE 0
 #endif
 #if DIT_CLOCK_PROBE
 constexpr int kClockProbeWgs = 4096;
-__device__ unsigned long long g_clock_probe[kClockProbeWgs * 4];
+__device__ unsigned long long g_clock_probe[kClockProbeWgs * 8];
 #endif
 __device__ __forceinline__ void clock_mark(int k) {
 #if DIT_CLOCK_PROBE
   if (threadIdx.x == 0 && blockIdx.x < kClockProbeWgs) {
-    g_clock_probe[blockIdx.x * 4 + 2 * k] = __builtin_amdgcn_s_memtime();
-    g_clock_probe[blockIdx.x * 4 + 2 * k + 1] = __builtin_amdgcn_s_memrealtime();
+    g_clock_probe[blockIdx.x * 8 + 2 * k] = __builtin_amdgcn_s_memtime();
+    g_clock_probe[blockIdx.x * 8 + 2 * k + 1] = __builtin_amdgcn_s_memrealtime();
   }
+#else
+  (void)k;
+#endif
+}
+// k = 0: workgroup entry; k = 1: after the workgroup's stores completed
+__device__ __forceinline__ void clock_edge(int k) {
+#if DIT_CLOCK_PROBE
+  if (k == 1) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are done
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && blockIdx.x < kClockProbeWgs)
+    g_clock_probe[blockIdx.x * 8 + 4 + k] = __builtin_amdgcn_s_memrealtime();
 #else
   (void)k;
 #endif
@@ -808,6 +824,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * G::TILE_BYTES];
   __shared__ int last_flag;
 
+  if (!STREAMK) clock_edge(0);
   Lane<D> ln;
   make_lane<D>(p, threadIdx.x, ln);
 
@@ -837,6 +854,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
     const float l_tot = pair_sum(l_run);
     const bool row_ok = query_is_real(p, qrow) && (nk > 0);
     store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
+    clock_edge(1);
     return;
   }
 
@@ -1101,9 +1119,10 @@ int attn_block_m() { return BM; }
 }  // namespace dit
 
 #if DIT_CLOCK_PROBE
-// Probe build only: copy the stamps of the last launch (4 words per
+// Probe build only: copy the stamps of the last launch (8 words per
 // workgroup: shader clock and 100 MHz counter at loop start, then at loop
-// end) to host memory; returns a hipError_t.
+// end; 100 MHz counter at entry and after the stores; two unused) to host
+// memory; returns a hipError_t.
 extern "C" __attribute__((visibility("default"))) int dit_clock_probe_read(unsigned long long *host) {
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(dit::g_clock_probe), sizeof(dit::g_clock_probe), 0,
                                   hipMemcpyDeviceToHost);
