@@ -503,15 +503,20 @@ def clock_probe(args):
     dev = torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     res = {"library": os.path.basename(Bld.LIB_CLOCK_PROBE), "compute_units": cus}
-    for name in ("wan480", "flux", "hunyuan", "wan720"):
+    for name, sched in (("wan480", 1), ("flux", 1), ("hunyuan", 1), ("wan720", 1), ("wan480", 2)):
         w = W.WORKLOADS[name]
         _, (qd, kd, vd) = dev_tensors(w, np, torch, dev)
         o = torch.empty_like(qd)
         lse = torch.empty((w.B, w.H, w.s_pad), dtype=torch.float32, device=dev)
-        fn = lambda: ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, out=o, lse=lse, schedule=1,
-                                  fixed_m=False)
+        ws = torch.empty(max(256, ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
+                                                          schedule=sched, fixed_m=False)),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda: ops.attn_fwd(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, out=o, lse=lse,
+                                  schedule=sched, fixed_m=False, workspace=ws)
         time_us(torch, fn, 1, warm_s=1.0)
         nwg = w.B * w.H * (-(-w.s_pad // 256))
+        if sched == 2:   # the split grid: one workgroup per CU at most
+            nwg = min(cus, nwg * (-(-w.k_valid // 64)))
         nk = -(-w.k_valid // 64)
         buf = np.zeros(4096 * 8, dtype=np.uint64)
         rounds = []
@@ -523,13 +528,19 @@ def clock_probe(args):
             b = buf[:min(nwg, 4096) * 8].reshape(-1, 8).astype(np.float64)
             cyc, real = b[:, 2] - b[:, 0], b[:, 3] - b[:, 1]
             mhz = cyc / real * 100.0
+            tiles = np.maximum(b[:, 6], 1)   # key tiles of the stamped loop
             ent = {"workgroups": int(len(b)), "key_tiles": nk, "loop_us_median": float(np.median(real) / 100),
                    "loop_cycles_median": float(np.median(cyc)), "mhz_median": float(np.median(mhz)),
                    "mhz_min": float(mhz.min()), "mhz_max": float(mhz.max()),
-                   "cycles_per_mfma_median": float(np.median(cyc) / (nk * 64))}
+                   "cycles_per_mfma_median": float(np.median(cyc / (tiles * 64)))}
+            if sched == 2:
+                ent["stamped_tiles_min_max"] = [int(b[:, 6].min()), int(b[:, 6].max())]
             # the last call's launch: workgroup entry (word 4) to loop start,
             # loop end to stores complete (word 5), and the span from the
             # first entry to the last exit against the per-call time
+            if sched == 2:   # no entry / exit stamps under the split schedule
+                rounds.append(ent)
+                continue
             entry, exit_ = b[:, 4], b[:, 5]
             ent.update({"call_us": call_us, "span_us": float((exit_.max() - entry.min()) / 100),
                         "entry_spread_us": float((entry.max() - entry.min()) / 100),
@@ -549,7 +560,7 @@ def clock_probe(args):
                 ent["mhz_median_later"] = float(np.median(mhz[~first])) if (~first).any() else None
                 ent["first_wave_workgroups"] = int(first.sum())
             rounds.append(ent)
-        res[name] = rounds
+        res[name if sched == 1 else name + "_split"] = rounds
         del qd, kd, vd, o
         torch.cuda.empty_cache()
     print(json.dumps({"clock_probe": res}), flush=True)

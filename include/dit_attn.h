@@ -70,9 +70,12 @@ typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
  * workgroup per query tile on the keys' head (all in step, so each K/V tile
  * is read while it is in L2) and lets the spare compute units split the
  * remaining key tails. AUTO resolves to PER_QTILE: on MI355X the split
- * measured slower on every shape tried (the chip is power-limited, so the
- * clock falls as the spare compute units join, and the partial results'
- * store and merge cost more than the shorter key range saves). */
+ * measured slower on every shape tried. Its loop over pieces leaves the
+ * kernel short of registers (spilled scalar and vector registers), so its
+ * key loop issues MFMAs about 30% slower than PER_QTILE's; and the chip is
+ * power-limited, so even at PER_QTILE's rate the clock falls as the spare
+ * compute units join, which leaves less to gain than the partial results'
+ * store and merge cost. */
 typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED = 2 } dit_schedule;
 
 /*

@@ -195,11 +195,14 @@ SplitPlan split_plan(int64_t nq, int64_t nk, int64_t cus) {
   return sp;
 }
 // AUTO never takes the split: on MI355X it measured slower on every shape
-// tried. The chip is power-limited, so the shader clock falls from about
-// 1.9 GHz with the Wan 480p shard's 190 q-tiles to about 1.65 GHz with every
-// CU busy, which cancels most of the shorter key range; and each piece's
-// device-scope partial store (3.5-6 us) and merge (about 9 us) cost more
-// than the rest saves (Wan 480p: 144 against 112 us per kernel).
+// tried (Wan 480p: 130 against 109 us per kernel). The split kernel's loop
+// over pieces costs it spilled registers, and its key loop runs 56.5
+// cycles per MFMA against 43.6 in the one-workgroup-per-q-tile kernel.
+// Even at that rate it would gain little: the chip is power-limited, and
+// with every CU busy at full MFMA rate the clock falls from about 2.1 GHz
+// (the Wan 480p shard's 190 q-tiles) to about 1.7 GHz, so 256 CUs deliver
+// only about 10% more than 190, before each piece's partial store and each
+// q-tile's merge.
 bool split_pays(int64_t, int64_t, int64_t) { return false; }
 
 // Compute units of the current device, or 0 when it cannot be queried (AUTO

@@ -82,13 +82,15 @@ __device__ __forceinline__ u32x4 ldg16(const bf16_t *p) { return *reinterpret_ca
 #endif
 // Clock probe build (compiled with -DDIT_CLOCK_PROBE=1 into a separate
 // library): the first thread of each of the first kClockProbeWgs workgroups
-// of the one-workgroup-per-q-tile kernel records the shader-clock counter
-// (s_memtime) and the constant 100 MHz counter (s_memrealtime) when its key
-// loop starts and when it ends (words 0-3 of its 8), and the 100 MHz
-// counter when the workgroup starts (word 4) and once every wave's O / LSE
-// stores have completed (word 5). Clock = loop cycles / loop time; the
-// entry and exit stamps place the prologue, the epilogue and the time
-// outside the workgroups in the launch. The arithmetic is unchanged.
+// records the shader-clock counter (s_memtime) and the constant 100 MHz
+// counter (s_memrealtime) when its key loop starts and when it ends (words
+// 0-3 of its 8) and the loop's key-tile count (word 6); in the
+// one-workgroup-per-q-tile kernel also the 100 MHz counter when the
+// workgroup starts (word 4) and once every wave's O / LSE stores have
+// completed (word 5). Under the split schedule the stamps are of the
+// workgroup's last piece. Clock = loop cycles / loop time; the entry and
+// exit stamps place the prologue, the epilogue and the time outside the
+// workgroups in the launch. The arithmetic is unchanged.
 #ifndef DIT_CLOCK_PROBE
 #define DIT_CLOCK_PROBE 0
 #endif
@@ -104,6 +106,14 @@ __device__ __forceinline__ void clock_mark(int k) {
   }
 #else
   (void)k;
+#endif
+}
+// the number of key tiles the stamped loop ran (word 6)
+__device__ __forceinline__ void clock_note_tiles(int n) {
+#if DIT_CLOCK_PROBE
+  if (threadIdx.x == 0 && blockIdx.x < kClockProbeWgs) g_clock_probe[blockIdx.x * 8 + 6] = (unsigned long long)n;
+#else
+  (void)n;
 #endif
 }
 // k = 0: workgroup entry; k = 1: after the workgroup's stores completed
@@ -851,6 +861,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
       for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
     }
     clock_mark(1);
+    clock_note_tiles(nk);
     const float l_tot = pair_sum(l_run);
     const bool row_ok = query_is_real(p, qrow) && (nk > 0);
     store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
@@ -893,6 +904,8 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
     const int h = bh % p.H, b = bh / p.H;
     const int qrow = qt * BM + ln.wave * 32 + ln.l32;
     run_qtile<D>(p, smem, ln, b, h, qt, kb, ke, acc_o, m_run, l_run);
+    clock_mark(1);
+    clock_note_tiles(ke - kb);
     const float l_tot = pair_sum(l_run);
     const float lse2 = m_run + __log2f(l_tot);
     const bool row_ok = query_is_real(p, qrow);
@@ -1121,8 +1134,8 @@ int attn_block_m() { return BM; }
 #if DIT_CLOCK_PROBE
 // Probe build only: copy the stamps of the last launch (8 words per
 // workgroup: shader clock and 100 MHz counter at loop start, then at loop
-// end; 100 MHz counter at entry and after the stores; two unused) to host
-// memory; returns a hipError_t.
+// end; 100 MHz counter at entry and after the stores; the loop's key
+// tiles; one unused) to host memory; returns a hipError_t.
 extern "C" __attribute__((visibility("default"))) int dit_clock_probe_read(unsigned long long *host) {
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(dit::g_clock_probe), sizeof(dit::g_clock_probe), 0,
                                   hipMemcpyDeviceToHost);
