@@ -595,6 +595,50 @@ __device__ __forceinline__ void store_final(const P &p, int b, int h, int qrow, 
   if (p.lse != nullptr && hf == 0) p.lse[((int64_t)b * p.H + h) * p.s_q + qrow] = row_ok ? lse2 * kLn2 : -INFINITY;
 }
 
+// Final epilogue of a whole q-tile with bf16 O, staged through LDS: each
+// wave writes its 32 x D block of O into its own slice of the tile buffers
+// (idle once every wave has finished the last tile), then reads it back so
+// that 16 lanes hold one row's D * 2 contiguous bytes and every store
+// instruction writes whole rows, instead of 16-byte pieces of 32 rows. The
+// 16-byte chunks of a row sit XOR-swizzled by the row in LDS, so neither
+// the writes nor the reads conflict. Pad rows are written as 0 and their
+// LSE as -inf; rows past s_q are not written. All threads of the workgroup
+// must call it (it has a barrier).
+template <int D, class P>
+__device__ __forceinline__ void store_final_staged(const P &p, char *smem, const Lane<D> &ln, int b, int h, int qt,
+                                                   const f32x16 *acc_o, float lse2, float inv_l, bool row_ok) {
+  constexpr int DB = D / 32, CPR = D / 8, ROWB = D * 2;
+  char *slice = smem + ln.wave * (32 * ROWB);
+  __syncthreads();   // every wave is done reading the last K / V tiles
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // this lane's channels db*32 + 8i + 4hf .. +3 of row l32: chunk db*4 + i
+      const int j = db * 4 + i;
+      float o4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = row_ok ? acc_o[db][4 * i + e] * inv_l : 0.0f;
+      *reinterpret_cast<u32x2 *>(slice + ln.l32 * ROWB + ((j ^ (ln.l32 % CPR)) * 16) + ln.hf * 8) =
+          u32x2{pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const int row0 = qt * BM + ln.wave * 32;
+  bf16_t *obase = reinterpret_cast<bf16_t *>(p.o) + b * p.os_b + h * p.os_h;
+#pragma unroll
+  for (int k = 0; k < 32 * CPR / 64; ++k) {
+    const int c = k * 64 + ln.lane;
+    const int r = c / CPR, j = c % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(slice + r * ROWB + ((j ^ (r % CPR)) * 16));
+    if (row0 + r < p.s_q) *reinterpret_cast<u32x4 *>(obase + (int64_t)(row0 + r) * p.os_s + j * 8) = v;
+  }
+  const int qrow = row0 + ln.l32;
+  if (p.lse != nullptr && ln.hf == 0 && qrow < p.s_q)
+    p.lse[((int64_t)b * p.H + h) * p.s_q + qrow] = row_ok ? lse2 * kLn2 : -INFINITY;
+}
+
 // Partials of split q-tiles move between workgroups that may sit on
 // different XCDs (separate L2s), so they are written and read with the
 // device-scope cache policy (sc1): such a store is complete at the device's
@@ -864,7 +908,11 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
     clock_note_tiles(nk);
     const float l_tot = pair_sum(l_run);
     const bool row_ok = query_is_real(p, qrow) && (nk > 0);
-    store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
+    if (p.o_f32)
+      store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
+    else
+      store_final_staged<D>(p, smem, ln, b, h, qt, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f,
+                            row_ok);
     clock_edge(1);
     return;
   }
@@ -991,7 +1039,11 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_seg_kernel(AttnParams p
   }
   const float l_tot = pair_sum(l_run);
   const bool row_ok = query_is_real(p, qrow) && (tps > 0);
-  store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
+  if (p.o_f32)
+    store_final<D>(p, b, h, qrow, ln.hf, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f, row_ok);
+  else
+    store_final_staged<D>(p, smem, ln, b, h, qt, acc_o, m_run + __log2f(l_tot), row_ok ? 1.0f / l_tot : 0.f,
+                          row_ok);
 }
 
 // Pre-pass of Q and K (blockIdx.y picks the tensor): optional per-head RMS
