@@ -198,11 +198,11 @@ SplitPlan split_plan(int64_t nq, int64_t nk, int64_t cus) {
 // tried (Wan 480p: 130 against 109 us per kernel). The split kernel's loop
 // over pieces costs it spilled registers, and its key loop runs 56.5
 // cycles per MFMA against 43.6 in the one-workgroup-per-q-tile kernel.
-// Even at that rate it would gain little: the chip is power-limited, and
-// with every CU busy at full MFMA rate the clock falls from about 2.1 GHz
-// (the Wan 480p shard's 190 q-tiles) to about 1.7 GHz, so 256 CUs deliver
-// only about 10% more than 190, before each piece's partial store and each
-// q-tile's merge.
+// Even with its loop at the per-q-tile rate it would gain little: the chip
+// is power-limited, and with every CU busy at full MFMA rate the clock
+// falls from about 2.1 GHz (the Wan 480p shard's 190 q-tiles) to about
+// 1.7 GHz, so 256 CUs deliver only about 9% more than 190, before each
+// piece's partial store and each q-tile's merge.
 bool split_pays(int64_t, int64_t, int64_t) { return false; }
 
 // Compute units of the current device, or 0 when it cannot be queried (AUTO

@@ -600,10 +600,11 @@ __device__ __forceinline__ void store_final(const P &p, int b, int h, int qrow, 
 // (idle once every wave has finished the last tile), then reads it back so
 // that 16 lanes hold one row's D * 2 contiguous bytes and every store
 // instruction writes whole rows, instead of 16-byte pieces of 32 rows. The
-// 16-byte chunks of a row sit XOR-swizzled by the row in LDS, so neither
-// the writes nor the reads conflict. Pad rows are written as 0 and their
-// LSE as -inf; rows past s_q are not written. All threads of the workgroup
-// must call it (it has a barrier).
+// 16-byte chunks of a row sit XOR-swizzled by the row in LDS; the 8 KB
+// each wave writes and reads back cost 64 bank-conflict cycles per wave
+// (SQ_LDS_BANK_CONFLICT), small next to the stores this saves. Pad rows
+// are written as 0 and their LSE as -inf; rows past s_q are not written.
+// All threads of the workgroup must call it (it has a barrier).
 template <int D, class P>
 __device__ __forceinline__ void store_final_staged(const P &p, char *smem, const Lane<D> &ln, int b, int h, int qt,
                                                    const f32x16 *acc_o, float lse2, float inv_l, bool row_ok) {
