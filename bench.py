@@ -664,6 +664,15 @@ def config_table(np, torch, ops, W, dev, n_iter, inputs=None, refs=None):
                                                                    workspace=wsv, **extra), n, warm_s=0.3)
                     del wsv
             del k_rot, q_rot
+        if name in ("flux", "wan480", "hunyuan", "wan720"):   # the placement forced each way (AUTO:
+            for tag, sc in (("per_qtile_us", 1), ("dynamic_us", 3)):   # dynamic from 4 waves of q-tiles)
+                wsd = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,
+                                                              rope_q=tabs, rope_k=tabs, schedule=sc), 256),
+                                  dtype=torch.uint8, device=dev)
+                ent[tag] = time_us(torch, lambda: ops.attn_fwd(
+                    qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid, rope_q=tabs, rope_k=tabs, out=o, lse=lse,
+                    workspace=wsd, schedule=sc), n, warm_s=0.3)
+                del wsd
         if name in ("wan480", "hunyuan", "wan720"):   # the softmax forced each way (AUTO: fixed-m from 32768 keys)
             for tag, fm in (("fixed_m_us", True), ("online_us", False)):
                 wsf = torch.empty(max(ops.attn_workspace_size(qd, kd, vd, q_valid=w.s_valid, kv_valid=w.k_valid,

@@ -69,14 +69,33 @@ typedef enum { DIT_BF16 = 0, DIT_F32 = 1 } dit_dtype;
  * With fewer query tiles than compute units, BALANCED keeps one "main"
  * workgroup per query tile on the keys' head (all in step, so each K/V tile
  * is read while it is in L2) and lets the spare compute units split the
- * remaining key tails. AUTO resolves to PER_QTILE: on MI355X the split
+ * remaining key tails. AUTO never takes BALANCED: on MI355X the split
  * measured slower on every shape tried. Its loop over pieces leaves the
  * kernel short of registers (spilled scalar and vector registers), so its
  * key loop issues MFMAs about 30% slower than PER_QTILE's; and the chip is
  * power-limited, so even at PER_QTILE's rate the clock falls as the spare
  * compute units join, which leaves less to gain than the partial results'
- * store and merge cost. */
-typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED = 2 } dit_schedule;
+ * store and merge cost.
+ * DYNAMIC keeps one workgroup per query tile but lets the workgroups take
+ * their tiles at run time: the tiles, in (b, h, tile) order, form eight
+ * queues (those PER_QTILE places on each of the eight XCDs), a workgroup
+ * takes the next tile of its own XCD's queue, else of the others, through
+ * device-scope counters in the workspace, and the grid has a sixteenth more
+ * workgroups than tiles (the spares exit when every queue is empty). The
+ * XCDs of an MI355X each run at their own clock under the power limit, so
+ * with several waves of tiles the XCDs that get through their queue first
+ * take over tiles the slower ones have not started. Each tile is computed
+ * exactly as under PER_QTILE, so the results are the same bits. Calls with
+ * key segments run PER_QTILE. AUTO resolves to DYNAMIC from four waves of
+ * query tiles (four per compute unit), else to PER_QTILE: with fewer waves
+ * the counters' contention when a wave starts costs more than the
+ * rebalancing saves. */
+typedef enum {
+  DIT_SCHED_AUTO = 0,
+  DIT_SCHED_PER_QTILE = 1,
+  DIT_SCHED_BALANCED = 2,
+  DIT_SCHED_DYNAMIC = 3
+} dit_schedule;
 
 /*
  * Attention forward descriptor.
@@ -111,18 +130,19 @@ typedef enum { DIT_SCHED_AUTO = 0, DIT_SCHED_PER_QTILE = 1, DIT_SCHED_BALANCED =
  *
  * workspace: device scratch for the once-per-call rotated (and normalised)
  * copies of K and Q (dense bf16 [B, H, s, d] each, when their tables or norm
- * weights are given), under the BALANCED schedule (also when AUTO picks it)
- * two fp32 partial-result slots per workgroup (2 * CUs * (256 KB / 128 * d
- * + 1 KB)) and one int32 arrival counter per query tile, and with fixed_m
+ * weights are given), under the BALANCED schedule two fp32 partial-result
+ * slots per workgroup (2 * CUs * (256 KB / 128 * d + 1 KB)) and one int32
+ * arrival counter per query tile, under DYNAMIC (also when AUTO picks it)
+ * nine int32 counters (256 bytes), and with fixed_m
  * the key and query statistics (fp32, about B*H*(s_q + 2*d + s_kv*d/256)
  * values). Required (non-NULL, 256-byte aligned, at least
  * dit_attn_workspace_size() bytes) when that size is non-zero. The caller
  * owns it; its contents need not be initialised. Calls that share one
  * workspace must not overlap.
  *
- * ws_counters_zero: the BALANCED schedule's arrival counters must be zero
- * when the attention kernel starts, and every completed call leaves them
- * zero. With 0 the call clears them (inside the Q/K pre-pass when one runs,
+ * ws_counters_zero: the BALANCED schedule's arrival counters and the
+ * DYNAMIC schedule's queue counters must be zero when the attention kernel
+ * starts, and every completed call leaves them zero. With 0 the call clears them (inside the Q/K pre-pass when one runs,
  * else with one small fill kernel). With 1 the caller guarantees they are
  * zero because the workspace comes unchanged from an earlier completed call
  * with the same arguments, and the clear is skipped.

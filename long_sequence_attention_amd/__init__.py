@@ -131,7 +131,9 @@ def attn_fwd(q, k, v, *, q_valid=None, kv_valid=None, rope_q=None, rope_k=None, 
     with d contiguous (e.g. a permuted [B, S, H, d] buffer). Rows >= q_valid /
     kv_valid are tail pads. rope_q / rope_k: (cos, sin) fp32 [S, d/2] tables
     or None. schedule: 0 auto, 1 one workgroup per query tile, 2 balanced
-    (Stream-K: one workgroup per compute unit).
+    (split key ranges, Stream-K style), 3 dynamic (one workgroup per query
+    tile, tiles taken at run time from per-XCD queues; auto from four query
+    tiles per compute unit).
     q_norm / k_norm: fp32 [d] RMSNorm weights (per-head q/k RMS normalisation
     before RoPE, epsilon norm_eps) or None. q_seg_len / kv_seg_len > 0: the
     rows form segments of that length, each padded at its own tail, and

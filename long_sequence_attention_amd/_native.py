@@ -19,6 +19,7 @@ DIT_F32 = 1
 DIT_SCHED_AUTO = 0
 DIT_SCHED_PER_QTILE = 1
 DIT_SCHED_BALANCED = 2
+DIT_SCHED_DYNAMIC = 3
 
 EXPORTED = (
     "dit_attn_workspace_size",

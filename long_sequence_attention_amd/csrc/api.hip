@@ -135,6 +135,8 @@ struct AttnPlan {
   size_t q_bytes = 0;       // prepared Q, dense [B, H, s_q, d] bf16 (after K)
   int sk_grid = 0;          // split-schedule workgroups (0 = one workgroup per q-tile)
   int sk_main = 0, sk_kc = 0;
+  int dyn_grid = 0;         // dynamic placement: workgroups (q-tiles plus spares; 0 = off)
+  int dyn_static = 0;       // ... of which the first wave, placed by index
   size_t part_o_off = 0, part_l_off = 0, count_off = 0;
   int64_t n_counts = 0;
   // fixed-m statistics (fm = false: online softmax)
@@ -145,6 +147,7 @@ struct AttnPlan {
 };
 
 constexpr int kBlockM = dit::kAttnBlockM, kBlockN = dit::kAttnBlockN, kThreads = dit::kAttnThreads;
+constexpr int64_t kDynMinWaves = 4;   // AUTO's dynamic placement: from this many waves of q-tiles
 
 // Split schedule for nq q-tiles of nk key tiles on `cus` compute units
 // (one workgroup per CU). Two shapes, modelled in tile-steps, the cheaper
@@ -194,16 +197,6 @@ SplitPlan split_plan(int64_t nq, int64_t nk, int64_t cus) {
   }
   return sp;
 }
-// AUTO never takes the split: on MI355X it measured slower on every shape
-// tried (Wan 480p: 130 against 109 us per kernel). The split kernel's loop
-// over pieces costs it spilled registers, and its key loop runs 56.5
-// cycles per MFMA against 43.6 in the one-workgroup-per-q-tile kernel.
-// Even with its loop at the per-q-tile rate it would gain little: the chip
-// is power-limited, and with every CU busy at full MFMA rate the clock
-// falls from about 2.1 GHz (the Wan 480p shard's 190 q-tiles) to about
-// 1.7 GHz, so 256 CUs deliver only about 9% more than 190, before each
-// piece's partial store and each q-tile's merge.
-bool split_pays(int64_t, int64_t, int64_t) { return false; }
 
 // Compute units of the current device, or 0 when it cannot be queried (AUTO
 // then keeps one workgroup per q-tile). Cached per device id.
@@ -242,19 +235,43 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
     p.q_bytes = round_up((size_t)d->B * d->H * (size_t)d->s_q * d->d * 2, 256);
   const int64_t nq = (int64_t)d->B * d->H * ((d->s_q + kBlockM - 1) / kBlockM);
   const int64_t nk = (d->kv_valid + kBlockN - 1) / kBlockN;
-  if (d->schedule < DIT_SCHED_AUTO || d->schedule > DIT_SCHED_BALANCED)
+  if (d->schedule < DIT_SCHED_AUTO || d->schedule > DIT_SCHED_DYNAMIC)
     return fail(DIT_ERR_INVALID, "schedule=%d is not a dit_schedule", d->schedule);
   // the split schedule covers plain (one-segment, online-softmax) calls with
   // at least two key tiles when BALANCED asks for it (see split_pays for AUTO)
-  if (d->schedule != DIT_SCHED_PER_QTILE && nq > 0 && nk >= 2 && d->kv_seg_len == 0 && !fm) {
+  // AUTO never takes the split: on MI355X it measured slower on every shape
+  // tried (Wan 480p: 130 against 109 us per kernel). The split kernel's loop
+  // over pieces costs it spilled registers, and its key loop runs 56.5
+  // cycles per MFMA against 43.6 in the one-workgroup-per-q-tile kernel.
+  // Even with its loop at the per-q-tile rate it would gain little: the chip
+  // is power-limited, and with every CU busy at full MFMA rate the clock
+  // falls from about 2.1 GHz (the Wan 480p shard's 190 q-tiles) to about
+  // 1.7 GHz, so 256 CUs deliver only about 9% more than 190, before each
+  // piece's partial store and each q-tile's merge.
+  if (d->schedule == DIT_SCHED_BALANCED && nq > 0 && nk >= 2 && d->kv_seg_len == 0 && !fm) {
     const int cus = device_cus();
-    if (cus <= 0 && d->schedule == DIT_SCHED_BALANCED)
+    if (cus <= 0) return fail(DIT_ERR_HIP, "cannot query the compute-unit count of the current device");
+    const SplitPlan sp = split_plan(nq, nk, cus);
+    p.sk_grid = sp.grid;
+    p.sk_main = sp.main;
+    p.sk_kc = sp.kc;
+  }
+  // dynamic placement: every call without key segments. AUTO takes it from
+  // kDynMinWaves waves of q-tiles: Wan 720p (2960 q-tiles, 11.6 waves)
+  // measured 23.6-23.8 against 24.3-24.5 ms per kernel, while FLUX (432,
+  // 1.7 waves) lost 11% (its second wave starts at once, and the contended
+  // counters delay it more than the few tiles to rebalance save). The spare
+  // workgroups are about what the fastest XCDs can take over (the XCDs'
+  // clocks differ by about 5%).
+  if ((d->schedule == DIT_SCHED_DYNAMIC || d->schedule == DIT_SCHED_AUTO) && nq > 0 && d->kv_seg_len == 0) {
+    const int cus = device_cus();
+    if (cus <= 0 && d->schedule == DIT_SCHED_DYNAMIC)
       return fail(DIT_ERR_HIP, "cannot query the compute-unit count of the current device");
-    if (cus > 0 && (d->schedule == DIT_SCHED_BALANCED || split_pays(nq, nk, cus))) {
-      const SplitPlan sp = split_plan(nq, nk, cus);
-      p.sk_grid = sp.grid;
-      p.sk_main = sp.main;
-      p.sk_kc = sp.kc;
+    if (cus > 0 && (d->schedule == DIT_SCHED_DYNAMIC || nq >= kDynMinWaves * (int64_t)cus)) {
+      const int64_t spare = nq / 16 > 8 ? nq / 16 : 8;
+      if (nq + spare > INT32_MAX) return fail(DIT_ERR_UNSUPPORTED, "too many query tiles for one launch");
+      p.dyn_grid = (int)(nq + spare);
+      p.dyn_static = p.dyn_grid < cus ? p.dyn_grid : cus;
     }
   }
   size_t off = p.k_bytes + p.q_bytes;
@@ -267,6 +284,11 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
     p.count_off = off;
     p.n_counts = nq;
     off += round_up((size_t)nq * sizeof(int32_t), 256);
+  }
+  if (p.dyn_grid > 0) {   // eight queue counters and the taken counter
+    p.count_off = off;
+    p.n_counts = 9;
+    off += 256;
   }
   if (fm && d->kv_valid > 0 && d->s_q > 0) {
     const size_t bh = (size_t)d->B * d->H;
@@ -402,15 +424,17 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
   p.sk_grid = pl.sk_grid;
   p.sk_main = pl.sk_main;
   p.sk_kc = pl.sk_kc;
+  p.dyn_grid = pl.dyn_grid;
+  p.dyn_static = pl.dyn_static;
   if (pl.sk_grid > 0) {
     char *ws = static_cast<char *>(d.workspace);
     p.sk_part_o = reinterpret_cast<float *>(ws + pl.part_o_off);
     p.sk_part_l = reinterpret_cast<float *>(ws + pl.part_l_off);
-    p.sk_count = reinterpret_cast<int32_t *>(ws + pl.count_off);
   }
+  if (pl.n_counts > 0) p.sk_count = reinterpret_cast<int32_t *>(static_cast<char *>(d.workspace) + pl.count_off);
 
   // one pre-pass normalises and / or rotates K (valid rows) and Q (all rows)
-  // into the workspace, and clears the split schedule's arrival counters
+  // into the workspace, and clears the schedule's counters
   const bool prepass = pl.k_bytes + pl.q_bytes > 0;
   if (prepass) {
     dit::RopeRotateParams r{};
@@ -462,8 +486,8 @@ int dit_attn_fwd(const dit_attn_desc *desc, void *stream) {
     p.fm_m = f.m;
     p.fm_ok = f.ok;
   }
-  if (pl.sk_grid > 0 && !prepass && !d.ws_counters_zero) {
-    // arrival counters start at zero (a fill kernel, not a memset node)
+  if (pl.n_counts > 0 && !prepass && !d.ws_counters_zero) {
+    // schedule counters start at zero (a fill kernel, not a memset node)
     rc = hip_status(dit::launch_zero_i32(p.sk_count, pl.n_counts, st), "counter clear launch");
     if (rc != DIT_OK) return rc;
   }

@@ -872,7 +872,59 @@ __device__ __forceinline__ void make_lane(const P &p, int tid, Lane<D> &ln) {
   }
 }
 
-template <int D, bool STREAMK>
+// Dynamic placement of whole q-tiles: the q-tiles, in (b, h, tile) order,
+// form eight contiguous queues, queue x holding the tiles the static
+// placement puts on XCD x (so a queue's tiles share K / V in that XCD's L2);
+// workgroup i runs on XCD i % 8 (round-robin dispatch). The first
+// p.dyn_static workgroups (one wave: one per CU) take the head of their own
+// XCD's queue by index, with no atomics, so a launch does not start with
+// hundreds of workgroups contending for eight counters. Every later
+// workgroup takes the next tile of its own queue, else of the others in
+// turn, through the device-scope counters sk_count[0..7] (counting past the
+// static part); -1 when every queue is empty. The grid has spare
+// workgroups: the XCDs run at their own clocks under the power limit, and
+// those that get through their queue first take over tiles the slower ones
+// have not started. The last of the later workgroups to take (counted in
+// sk_count[8]) sets the nine counters back to zero for the next call.
+// Uniform over the workgroup (sh: a shared int for the broadcast).
+constexpr int kDynQueues = 8;
+
+template <class P>
+__device__ __forceinline__ int take_tile(const P &p, int &sh) {
+  const int total = p.n_qtiles * p.H * p.B;
+  const int q8 = total / kDynQueues, r8 = total % kDynQueues;
+  const int S = p.dyn_static;
+  const int bid = (int)blockIdx.x;
+  if (bid < S) {   // first wave: the head of its own queue, by index
+    const int x = bid % kDynQueues, idx = bid / kDynQueues;
+    const int start = x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8;
+    const int len = q8 + (x < r8 ? 1 : 0);
+    return idx < len ? start + idx : -1;
+  }
+  if (threadIdx.x == 0) {
+    int t = -1;
+    for (int k = 0; k < kDynQueues && t < 0; ++k) {
+      const int x = (bid + k) % kDynQueues;
+      const int start = x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8;
+      const int len = q8 + (x < r8 ? 1 : 0);
+      const int n_static = x < S ? (S - x + kDynQueues - 1) / kDynQueues : 0;   // taken by index
+      const int base = n_static < len ? n_static : len;
+      const int i = __hip_atomic_fetch_add(p.sk_count + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (i >= 0 && base + i < len) t = start + base + i;   // (i < 0 only if a caller broke the zero-counter contract)
+    }
+    const int taken =
+        __hip_atomic_fetch_add(p.sk_count + kDynQueues, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (taken == (int)gridDim.x - S - 1) {   // every other later workgroup has taken its tile (or found none)
+      for (int x = 0; x <= kDynQueues; ++x)
+        __hip_atomic_store(p.sk_count + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    sh = t;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(sh);
+}
+
+template <int D, bool STREAMK, bool DYN = false>
 __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   using G = Geo<D>;
   constexpr int DB = D / 32;
@@ -889,8 +941,15 @@ __global__ __launch_bounds__(NT, 512 / NT) void attn_fwd_kernel(AttnParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   if (!STREAMK) {
-    // one workgroup per q-tile, all key tiles
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    // one workgroup per q-tile, all key tiles; the q-tile is placed by the
+    // block index, or taken from the dynamic queues
+    int logical;
+    if (DYN) {
+      logical = take_tile(p, last_flag);
+      if (logical < 0) return;   // uniform: every queue was empty
+    } else {
+      logical = xcd_remap(blockIdx.x, gridDim.x);
+    }
     const int qt = logical % p.n_qtiles;
     const int bh = logical / p.n_qtiles;
     const int h = bh % p.H, b = bh / p.H;
@@ -1150,6 +1209,13 @@ hipError_t launch_attn_fwd(const AttnParams &p, int d, hipStream_t stream) {
     if (nb <= 0) return hipSuccess;
     if (d == 128) hipLaunchKernelGGL(attn_fwd_seg_kernel<128>, dim3((unsigned)nb), dim3(NT), 0, stream, p);
     else hipLaunchKernelGGL(attn_fwd_seg_kernel<64>, dim3((unsigned)nb), dim3(NT), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (p.dyn_grid > 0) {
+    if (d == 128)
+      hipLaunchKernelGGL((attn_fwd_kernel<128, false, true>), dim3((unsigned)p.dyn_grid), dim3(NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<64, false, true>), dim3((unsigned)p.dyn_grid), dim3(NT), 0, stream, p);
     return hipGetLastError();
   }
   const bool sk = p.sk_grid > 0;

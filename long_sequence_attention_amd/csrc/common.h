@@ -75,7 +75,12 @@ struct AttnParams {
   int32_t sk_grid, sk_main, sk_kc;
   float *sk_part_o;  // [2 sk_grid slots][kAttnThreads][d/2] partial O / l, fp32
   float *sk_part_l;  // [2 sk_grid slots][kAttnBlockM rows] partial LSE, log2 units
-  int32_t *sk_count; // [q-tiles] arrival counters, zero on entry (left zero on exit)
+  int32_t *sk_count; // [q-tiles] arrival counters, zero on entry (left zero on exit);
+                     // dynamic placement: [0..7] next tile of each XCD queue, [8] tiles taken
+  // dynamic placement (dyn_grid > 0 workgroups, more than the q-tiles; the
+  // first dyn_static take their q-tile by index, the rest through the
+  // sk_count queue counters; 0 = off)
+  int32_t dyn_grid, dyn_static;
   // fixed-m softmax (fm_m != nullptr): row bounds [B*H][s_q] and per-q-tile
   // flags [B*H][n_qtiles] from launch_fixed_m
   const float *fm_m;

@@ -404,7 +404,7 @@ def _random_case(seed):
              q_valid=int(r.integers(0, s_q + 1)), kv_valid=int(r.integers(0, s_kv + 1)),
              rope_q=bool(r.random() < 0.6), rope_k=bool(r.random() < 0.6), norm=bool(r.random() < 0.3),
              tok_layout=bool(r.random() < 0.5), f32_out=bool(r.random() < 0.3),
-             schedule=int(r.choice([0, 1, 2])), scale=float(r.choice([0.0, 0.05])))
+             schedule=int(r.choice([0, 1, 2, 3])), scale=float(r.choice([0.0, 0.05])))
     c["fixed_m"] = bool(c["schedule"] != 2 and r.random() < 0.4)
     return c
 
@@ -866,7 +866,8 @@ def test_no_valid_keys_gives_zero_and_minus_inf(ops):
     assert (to_np_f64(o) == 0).all() and np.isneginf(to_np_f64(l)).all()
 
 
-@pytest.mark.parametrize("case", ["wan480", "wan480_fixed_m", "wan480_balanced", "ring_2_segments", "tiny_d64"])
+@pytest.mark.parametrize("case", ["wan480", "wan480_fixed_m", "wan480_balanced", "wan480_dynamic", "ring_2_segments",
+                                  "tiny_d64"])
 def test_race_check_build_is_bit_identical(ops, case):
     """The race-check build of the library (a wait and a barrier after every
     DMA issue and LDS read phase of the attention kernel, same arithmetic)
@@ -891,6 +892,8 @@ def test_race_check_build_is_bit_identical(ops, case):
         kw["fixed_m"] = True
     if case == "wan480_balanced":
         kw["schedule"] = 2
+    if case == "wan480_dynamic":
+        kw["schedule"] = 3
     tabs = ops.rope_split_tables(torch.from_numpy(pos).to(dev()), w.axes, w.d, w.theta)
     qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
     o1, l1 = ops.attn_fwd(qd, kd, vd, rope_q=tabs, rope_k=tabs, **kw)
@@ -960,13 +963,19 @@ def test_pad_unpad_round_trip(ops):
     dict(name="flux", sched=2),
     dict(name="wan480", sched=1),
     dict(name="flux", sched=1),
+    dict(name="tiny", sched=3),
+    dict(name="wan480", sched=3),
+    dict(name="flux", sched=3),
 ])
 def test_forced_schedules_match_oracle(ops, case):
-    """Both work schedules against the oracle: one workgroup per query tile,
-    and the split (BALANCED) schedule, whose pieces meet in the workspace:
-    with fewer query tiles than CUs (tiny, HunyuanVideo, Wan 480p) main
-    workgroups plus helpers splitting the key tails, else (FLUX's 432 query
-    tiles) plain Stream-K over every unit."""
+    """Every work schedule against the oracle: one workgroup per query tile
+    placed by its block index; the split (BALANCED) schedule, whose pieces
+    meet in the workspace (with fewer query tiles than CUs, as for tiny,
+    HunyuanVideo and Wan 480p, main workgroups plus helpers splitting the
+    key tails, else, as for FLUX's 432 query tiles, plain Stream-K over
+    every unit); and the dynamic placement, workgroups taking whole query
+    tiles from per-XCD queues at run time (tiny: fewer tiles than queues;
+    Wan 480p: one wave; FLUX: 1.7 waves, so spare workgroups take tiles)."""
     import torch
     w = W.WORKLOADS[case["name"]]
     say(f"schedule {case['sched']} {w.name}")
@@ -981,6 +990,35 @@ def test_forced_schedules_match_oracle(ops, case):
     og, lg = to_np_f64(o), to_np_f64(l)
     compare(og, lg, O_ref, L_ref, valid, f"{w.name} schedule {case['sched']}")
     assert_pad_rows(og, lg, valid, "schedule")
+
+
+@pytest.mark.parametrize("fixed_m", [False, True])
+def test_dynamic_placement_is_bit_identical_to_per_qtile(ops, fixed_m):
+    """The dynamic placement computes every query tile exactly as the
+    block-index placement does, whichever workgroup takes it: on FLUX (432
+    query tiles, more than one wave) its O and LSE must equal PER_QTILE's
+    bits, on every one of three calls sharing one workspace that starts as
+    garbage (each call clears the queue counters, each leaves them zero),
+    and on a fourth call told the counters are already zero
+    (ws_counters_zero), with the outputs pre-filled with NaN each time."""
+    import torch
+    w = W.WORKLOADS["flux"]
+    say(f"dynamic vs per-qtile flux fixed_m={fixed_m}")
+    q, k, v = W.make_qkv(w)
+    tabs = gpu_tables(ops, w)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    kw = dict(q_valid=w.s_valid, kv_valid=w.s_valid, rope_q=tabs, rope_k=tabs, fixed_m=fixed_m)
+    o1, l1 = ops.attn_fwd(qd, kd, vd, schedule=1, **kw)
+    nbytes = ops.attn_workspace_size(qd, kd, vd, schedule=3, **kw)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=dev())   # garbage, not zeros
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    for i in range(4):
+        o2.fill_(float("nan"))
+        l2.fill_(float("nan"))
+        ops.attn_fwd(qd, kd, vd, schedule=3, workspace=ws, out=o2, lse=l2, ws_counters_zero=i == 3, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), (fixed_m, i)
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), (fixed_m, i)
 
 
 @pytest.mark.parametrize("kv_valid", [1000, 999, 129, 65])
