@@ -238,7 +238,7 @@ int plan_attn(const dit_attn_desc *d, AttnPlan *pl) {
   if (d->schedule < DIT_SCHED_AUTO || d->schedule > DIT_SCHED_DYNAMIC)
     return fail(DIT_ERR_INVALID, "schedule=%d is not a dit_schedule", d->schedule);
   // the split schedule covers plain (one-segment, online-softmax) calls with
-  // at least two key tiles when BALANCED asks for it (see split_pays for AUTO)
+  // at least two key tiles, only when BALANCED asks for it.
   // AUTO never takes the split: on MI355X it measured slower on every shape
   // tried (Wan 480p: 130 against 109 us per kernel). The split kernel's loop
   // over pieces costs it spilled registers, and its key loop runs 56.5

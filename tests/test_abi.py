@@ -84,6 +84,8 @@ def _desc(**kw):
     (dict(kv_seg_len=-1), -1, b"segment lengths"),
     (dict(fixed_m=3), -1, b"fixed_m"),
     (dict(ws_counters_zero=3), -1, b"ws_counters_zero"),
+    (dict(schedule=4), -1, b"schedule"),
+    (dict(schedule=-1), -1, b"schedule"),
 ])
 def test_attn_fwd_rejects_bad_arguments_before_any_hip_call(L, kw, code, msg):
     d = _desc(**kw)
