@@ -282,6 +282,29 @@ DIT_API int dit_rope_split_tables(const int32_t *pos, int S, int n_axes, const i
 DIT_API int dit_pad_tokens(const void *in, void *out, int B, int s_valid, int s_pad,
                    int64_t row_bytes, void *stream);
 
+/*
+ * Tail padding of fused token rows with the split-halves RoPE applied on the
+ * way (Difflet PR #153: Wan padding commit, 4680 -> 4736, and FLUX split-RoPE
+ * commit, x'_i = x_i c_i - x_{i+d/2} s_i, x'_{i+d/2} = x_{i+d/2} c_i + x_i s_i;
+ * the pages fuse the rotation into the neighbouring data movement).
+ * in:  device bf16 [B, s_valid, T, H, d], dense, token-major (what one
+ *      all-to-all of the stacked Q, K, V hands over: T = 3);
+ * out: device bf16 [B, s_pad, T, H, d], dense, owned by the caller.
+ * For every real row s < s_valid the head vectors of tensors t < n_rot (Q,
+ * then K) are rotated with row s of cos_t / sin_t (device fp32 [>= s_valid,
+ * d/2], as dit_rope_split_tables writes them) in fp32 and rounded once to
+ * bf16 (to nearest even), exactly as dit_attn_fwd's own pre-pass rotates;
+ * the other tensors are copied; rows >= s_valid of `out` are zero. Feeding
+ * `out` to dit_attn_fwd without tables therefore gives the same bits as
+ * dit_pad_tokens followed by dit_attn_fwd with the tables.
+ * DIT_ERR_INVALID: B < 1, s_valid < 0, s_pad < s_valid, T < 1, H < 1,
+ * n_rot outside [0, T], a required NULL pointer, in == out, a pointer not
+ * 16-byte aligned. DIT_ERR_UNSUPPORTED: d not in {64, 128}, B > 65535,
+ * T * H * d/16 * s_pad >= 2^31.
+ */
+DIT_API int dit_pad_tokens_rope(const void *in, void *out, int B, int s_valid, int s_pad, int T, int H, int d,
+                                int n_rot, const float *cos_t, const float *sin_t, void *stream);
+
 /* Inverse of dit_pad_tokens: in [B, s_pad, row_bytes] -> out [B, s_valid, row_bytes]
  * (no in-place operation; same status codes as dit_pad_tokens). */
 DIT_API int dit_unpad_tokens(const void *in, void *out, int B, int s_pad, int s_valid,

@@ -16,7 +16,7 @@ import torch
 from . import _native as N
 from ._native import DitError  # noqa: F401
 
-__all__ = ["attn_fwd", "attn_fwd_noalloc", "lse_merge", "rope_split_tables", "pad_tokens", "unpad_tokens",
+__all__ = ["attn_fwd", "attn_fwd_noalloc", "lse_merge", "rope_split_tables", "pad_tokens", "pad_tokens_rope", "unpad_tokens",
            "plan_padding", "library_path", "attn_workspace_size", "NOALLOC_SCRATCH_BYTES"]
 
 NOALLOC_SCRATCH_BYTES = 128 << 20   # DIT_NOALLOC_SCRATCH_BYTES
@@ -290,6 +290,31 @@ def pad_tokens(x, s_pad: int, out=None):
     with _on_device(x.device):
         N.check(N.lib().dit_pad_tokens(_ptr(x), _ptr(out), B, s_valid, int(s_pad), row_bytes, _stream(x.device)),
                 "pad_tokens")
+    return out
+
+
+def pad_tokens_rope(x, s_pad: int, cos, sin, n_rot: int = 2, out=None):
+    """Fused token rows [B, s_valid, T, H, d] (bf16, dense) -> [B, s_pad, T, H, d]
+    with zero tail rows, the head vectors of the first n_rot tensors of every
+    real row rotated (split halves) with row s of cos / sin (fp32 [>= s_valid,
+    d/2]) on the way (dit_pad_tokens_rope)."""
+    _need_cuda("x", x, torch.bfloat16)
+    if not x.is_contiguous() or x.dim() != 5:
+        raise ValueError("x must be a dense [B, s_valid, T, H, d] tensor")
+    B, s_valid, T, H, d = x.shape
+    _need_cuda("cos", cos, torch.float32)
+    _need_cuda("sin", sin, torch.float32)
+    _same_device(x.device, cos=cos, sin=sin)
+    for name, t in (("cos", cos), ("sin", sin)):
+        if t.dim() != 2 or t.shape[0] < s_valid or t.shape[1] != d // 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a dense fp32 [>= {s_valid}, {d // 2}] tensor")
+    if out is None:
+        out = torch.empty((B, int(s_pad), T, H, d), dtype=x.dtype, device=x.device)
+    else:
+        _check_out("out", out, (B, int(s_pad), T, H, d), (x.dtype,), x.device)
+    with _on_device(x.device):
+        N.check(N.lib().dit_pad_tokens_rope(_ptr(x), _ptr(out), B, s_valid, int(s_pad), T, H, d, int(n_rot),
+                                            _ptr(cos), _ptr(sin), _stream(x.device)), "pad_tokens_rope")
     return out
 
 

@@ -28,6 +28,7 @@ EXPORTED = (
     "dit_lse_merge",
     "dit_rope_split_tables",
     "dit_pad_tokens",
+    "dit_pad_tokens_rope",
     "dit_unpad_tokens",
     "dit_plan_padding",
     "dit_last_error",
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
     L.dit_rope_split_tables.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int32), i32, f32, vp, vp, vp]
     L.dit_pad_tokens.argtypes = [vp, vp, i32, i32, i32, i64, vp]
     L.dit_unpad_tokens.argtypes = [vp, vp, i32, i32, i32, i64, vp]
+    L.dit_pad_tokens_rope.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     L.dit_plan_padding.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int)]
     L.dit_last_error.argtypes = []
     L.dit_last_error.restype = ctypes.c_char_p

@@ -581,6 +581,35 @@ int dit_pad_tokens(const void *in, void *out, int B, int s_valid, int s_pad, int
                     "pad launch");
 }
 
+int dit_pad_tokens_rope(const void *in, void *out, int B, int s_valid, int s_pad, int T, int H, int d, int n_rot,
+                        const float *cos_t, const float *sin_t, void *stream) {
+  if (B < 1 || s_valid < 0 || s_pad < s_valid || T < 1 || H < 1 || n_rot < 0 || n_rot > T)
+    return fail(DIT_ERR_INVALID, "need B >= 1, 0 <= s_valid <= s_pad, T >= 1, H >= 1, 0 <= n_rot <= T");
+  if (d != 64 && d != 128) return fail(DIT_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (s_pad > 0 && out == nullptr) return fail(DIT_ERR_INVALID, "out is NULL");
+  if (s_valid > 0 && in == nullptr) return fail(DIT_ERR_INVALID, "in is NULL");
+  if (s_valid > 0 && n_rot > 0 && (cos_t == nullptr || sin_t == nullptr))
+    return fail(DIT_ERR_INVALID, "cos_t / sin_t are NULL with n_rot > 0");
+  if (in != nullptr && in == out) return fail(DIT_ERR_INVALID, "in and out must not alias");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out) |
+                       reinterpret_cast<uintptr_t>(cos_t) | reinterpret_cast<uintptr_t>(sin_t);
+  if (al % 16 != 0) return fail(DIT_ERR_INVALID, "in, out, cos_t and sin_t must be 16-byte aligned");
+  if (B > 65535) return fail(DIT_ERR_UNSUPPORTED, "B > 65535 (one grid row per batch)");
+  if ((int64_t)T * H * (d / 16) * s_pad >= (int64_t(1) << 31))
+    return fail(DIT_ERR_UNSUPPORTED, "T * H * d/16 * s_pad must be below 2^31");
+  dit::PadRopeParams p{};
+  p.in = static_cast<const dit::bf16_t *>(in);
+  p.out = static_cast<dit::bf16_t *>(out);
+  p.cos_t = cos_t;
+  p.sin_t = sin_t;
+  p.s_valid = s_valid;
+  p.s_pad = s_pad;
+  p.T = T;
+  p.H = H;
+  p.n_rot = n_rot;
+  return hip_status(dit::launch_pad_rope(p, B, d, reinterpret_cast<hipStream_t>(stream)), "pad+rope launch");
+}
+
 int dit_unpad_tokens(const void *in, void *out, int B, int s_pad, int s_valid, int64_t row_bytes, void *stream) {
   if (B < 1 || s_valid < 0 || s_pad < s_valid || row_bytes <= 0)
     return fail(DIT_ERR_INVALID, "need B >= 1, 0 <= s_valid <= s_pad, row_bytes > 0");

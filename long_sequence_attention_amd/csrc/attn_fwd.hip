@@ -137,30 +137,6 @@ __device__ __forceinline__ void debug_sync() {
   }
 }
 
-// Split-halves rotation of 8 channel pairs in fp32: x1 holds channels
-// i..i+7 of the first half, x2 the partners d/2 later.
-__device__ __forceinline__ void rotate8(float *x1, float *x2, const float *cv, const float *sv) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float y1 = fmaf(x1[e], cv[e], -x2[e] * sv[e]);
-    const float y2 = fmaf(x2[e], cv[e], x1[e] * sv[e]);
-    x1[e] = y1;
-    x2[e] = y2;
-  }
-}
-
-__device__ __forceinline__ void unpack8(const u32x4 &v, float *x) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    x[2 * w] = bf16_lo(v[w]);
-    x[2 * w + 1] = bf16_hi(v[w]);
-  }
-}
-
-__device__ __forceinline__ u32x4 pack8(const float *x) {
-  return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-}
-
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   const int xcd = bid & 7, idx = bid >> 3;
   const int q = nb >> 3, r = nb & 7;
@@ -1143,12 +1119,8 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(RopeRotateParams p) {
     float cv[8], sv[8];
     if (rot) {
       const int64_t to = (int64_t)s * HALF + c * 8;
-      const float4 c0 = *reinterpret_cast<const float4 *>(g.cos_t + to);
-      const float4 c1 = *reinterpret_cast<const float4 *>(g.cos_t + to + 4);
-      const float4 s0 = *reinterpret_cast<const float4 *>(g.sin_t + to);
-      const float4 s1 = *reinterpret_cast<const float4 *>(g.sin_t + to + 4);
-      cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w; cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
-      sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+      load8f(g.cos_t + to, cv);
+      load8f(g.sin_t + to, sv);
     }
     // all loads of the group first, then the arithmetic and stores
     u32x4 lo[kRopeHeads], hi[kRopeHeads];

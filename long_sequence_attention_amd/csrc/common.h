@@ -26,6 +26,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// Eight bf16 from one 16-byte word group -> fp32, and back (round to nearest even).
+__device__ __forceinline__ void unpack8(const u32x4 &v, float *x) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    x[2 * w] = bf16_lo(v[w]);
+    x[2 * w + 1] = bf16_hi(v[w]);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float *x) {
+  return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+}
+
+// Split-halves rotation of 8 channel pairs in fp32: x1 holds channels
+// i..i+7 of the first half, x2 the partners d/2 later. Every kernel that
+// rotates uses this one routine, so they all round alike.
+__device__ __forceinline__ void rotate8(float *x1, float *x2, const float *cv, const float *sv) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y1 = fmaf(x1[e], cv[e], -x2[e] * sv[e]);
+    const float y2 = fmaf(x2[e], cv[e], x1[e] * sv[e]);
+    x1[e] = y1;
+    x2[e] = y2;
+  }
+}
+
+// Eight consecutive fp32 table entries (32-byte aligned run).
+__device__ __forceinline__ void load8f(const float *t, float *x) {
+  const float4 a = *reinterpret_cast<const float4 *>(t);
+  const float4 b = *reinterpret_cast<const float4 *>(t + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 // Attention tiling shared by the kernels and the host planning code: a
 // workgroup of kAttnWaves waves owns kAttnBlockM = 32 * kAttnWaves query
 // rows of one head and walks the keys in tiles of kAttnBlockN rows.
@@ -111,6 +144,17 @@ struct RopeRotateParams {
   int32_t n_zero;
 };
 
+// Tail pad of fused token rows with the rotation on the way: in [B, s_valid,
+// T, H, d] -> out [B, s_pad, T, H, d] (dense, token-major), tensors t < n_rot
+// of every real row rotated with the fp32 [>= s_valid, d/2] tables, the
+// others copied, rows >= s_valid zero.
+struct PadRopeParams {
+  const bf16_t *in;
+  bf16_t *out;
+  const float *cos_t, *sin_t;
+  int32_t s_valid, s_pad, T, H, n_rot;
+};
+
 constexpr int kMaxMergeParts = 16;
 struct MergeParams {
   const void *o_parts[kMaxMergeParts];
@@ -138,5 +182,6 @@ hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 hipError_t launch_rope_tables(const TableParams &p, hipStream_t stream);
 hipError_t launch_row_copy(const void *in, void *out, int B, int s_in, int s_out, int n_copy,
                            int64_t row_bytes, hipStream_t stream);
+hipError_t launch_pad_rope(const PadRopeParams &p, int B, int d, hipStream_t stream);
 
 }  // namespace dit

@@ -2,7 +2,8 @@
 //   * RoPE cos/sin tables from integer positions (Difflet PR #153, FLUX
 //     split-RoPE commit: tables built once per forward, split-halves order);
 //   * tail pad / unpad of token rows (Difflet PR #153 Wan padding commit;
-//     maxdiffusion PR #491 lane padding);
+//     maxdiffusion PR #491 lane padding), and the pad of fused Q/K/V rows
+//     with the split-halves rotation of Q and K applied on the way;
 //   * the LSE merge of per-key-shard partial results (mstar PR #376,
 //     attention_over_sharded_keys).
 // Each is a streaming pass: 16-byte vector loads/stores, consecutive lanes on
@@ -122,6 +123,51 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
   if (p.lse_out != nullptr && sub == 0) p.lse_out[row] = empty ? -INFINITY : M + logf(wsum);
 }
 
+// Tail pad of fused token rows with the split-halves rotation applied on the
+// way: one pass over Q, K and V instead of a pad copy followed by a rotation
+// pass over Q and K (the pages fuse the rotation into neighbouring work). A
+// task is one 8-channel run of one head vector and its partner run d/2 later
+// (2 x 16 bytes); consecutive lanes take consecutive runs, so a wave reads and
+// writes whole rows. Head vectors of the first n_rot tensors of a real row are
+// rotated with that row's tables by rotate8, the routine of the attention
+// pre-pass, so the two paths give the same bits; the others are copied; pad
+// rows are written as zeros. (T * H * RUNS * s_pad < 2^31 is checked by the
+// caller, so the task index is 32-bit.)
+template <int RUNS>
+__global__ __launch_bounds__(256) void pad_rope_kernel(PadRopeParams p) {
+  constexpr int HALF = RUNS * 8;
+  const uint32_t vecs = (uint32_t)(p.T * p.H);
+  const uint32_t per_row = vecs * RUNS;
+  const uint32_t total = per_row * (uint32_t)p.s_pad;
+  const uint32_t n_rot_vecs = (uint32_t)(p.n_rot * p.H);
+  const int64_t row_elems = (int64_t)vecs * (2 * HALF);
+  const bf16_t *src = p.in + (int64_t)blockIdx.y * p.s_valid * row_elems;
+  bf16_t *dst = p.out + (int64_t)blockIdx.y * p.s_pad * row_elems;
+  for (uint32_t g = blockIdx.x * 256u + threadIdx.x; g < total; g += gridDim.x * 256u) {
+    const uint32_t s = g / per_row;
+    const uint32_t r = g - s * per_row;
+    const uint32_t vec = r / RUNS, c = r % RUNS;
+    const int64_t off = (int64_t)s * row_elems + (int64_t)vec * (2 * HALF) + c * 8;
+    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    if (s < (uint32_t)p.s_valid) {
+      lo = *reinterpret_cast<const u32x4 *>(src + off);
+      hi = *reinterpret_cast<const u32x4 *>(src + off + HALF);
+      if (vec < n_rot_vecs) {
+        float cv[8], sv[8], x1[8], x2[8];
+        load8f(p.cos_t + (int64_t)s * HALF + c * 8, cv);
+        load8f(p.sin_t + (int64_t)s * HALF + c * 8, sv);
+        unpack8(lo, x1);
+        unpack8(hi, x2);
+        rotate8(x1, x2, cv, sv);
+        lo = pack8(x1);
+        hi = pack8(x2);
+      }
+    }
+    *reinterpret_cast<u32x4 *>(dst + off) = lo;
+    *reinterpret_cast<u32x4 *>(dst + off + HALF) = hi;
+  }
+}
+
 int grid_for(int64_t total) {
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
@@ -172,6 +218,17 @@ hipError_t launch_row_copy(const void *in, void *out, int B, int s_in, int s_out
   if (row_bytes % 16 == 0 && a % 16 == 0) launch_copy_v<u32x4>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
   else if (row_bytes % 4 == 0 && a % 4 == 0) launch_copy_v<uint32_t>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
   else launch_copy_v<uint8_t>(in, out, B, s_in, s_out, n_copy, row_bytes, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_rope(const PadRopeParams &p, int B, int d, hipStream_t stream) {
+  const int64_t total = (int64_t)p.T * p.H * (d / 16) * p.s_pad;
+  if (total <= 0 || B <= 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65535) blocks = 65535;   // the kernel strides over the rest
+  const dim3 grid((unsigned)blocks, (unsigned)B);
+  if (d == 128) hipLaunchKernelGGL(pad_rope_kernel<8>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(pad_rope_kernel<4>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -150,6 +150,22 @@ int main() {
   expect("pad alias", dit_pad_tokens(a, a, 1, 5, 10, 256, nullptr), DIT_ERR_INVALID, "alias");
   expect("pad row_bytes", dit_pad_tokens(a, b, 1, 10, 16, 0, nullptr), DIT_ERR_INVALID, "row_bytes");
   expect("pad B huge", dit_pad_tokens(a, b, 70000, 10, 16, 256, nullptr), DIT_ERR_UNSUPPORTED, "65535");
+  {
+    const float *t = reinterpret_cast<const float *>(uintptr_t(0x30000000));
+    void *m = reinterpret_cast<void *>(uintptr_t(0x1008));
+    expect("pad+rope s_pad < s_valid", dit_pad_tokens_rope(a, b, 1, 10, 5, 3, 2, 128, 2, t, t, nullptr), DIT_ERR_INVALID, "s_valid");
+    expect("pad+rope n_rot > T", dit_pad_tokens_rope(a, b, 1, 10, 16, 3, 2, 128, 4, t, t, nullptr), DIT_ERR_INVALID, "n_rot");
+    expect("pad+rope T = 0", dit_pad_tokens_rope(a, b, 1, 10, 16, 0, 2, 128, 0, t, t, nullptr), DIT_ERR_INVALID, "T >= 1");
+    expect("pad+rope d", dit_pad_tokens_rope(a, b, 1, 10, 16, 3, 2, 96, 2, t, t, nullptr), DIT_ERR_UNSUPPORTED, "64 or 128");
+    expect("pad+rope alias", dit_pad_tokens_rope(a, a, 1, 10, 16, 3, 2, 128, 2, t, t, nullptr), DIT_ERR_INVALID, "alias");
+    expect("pad+rope NULL tables", dit_pad_tokens_rope(a, b, 1, 10, 16, 3, 2, 128, 2, nullptr, t, nullptr), DIT_ERR_INVALID, "cos_t");
+    expect("pad+rope NULL in", dit_pad_tokens_rope(nullptr, b, 1, 10, 16, 3, 2, 128, 2, t, t, nullptr), DIT_ERR_INVALID, "in is NULL");
+    expect("pad+rope NULL out", dit_pad_tokens_rope(a, nullptr, 1, 10, 16, 3, 2, 128, 2, t, t, nullptr), DIT_ERR_INVALID, "out is NULL");
+    expect("pad+rope misaligned", dit_pad_tokens_rope(m, b, 1, 10, 16, 3, 2, 128, 2, t, t, nullptr), DIT_ERR_INVALID, "16-byte");
+    expect("pad+rope B huge", dit_pad_tokens_rope(a, b, 70000, 10, 16, 3, 2, 128, 2, t, t, nullptr), DIT_ERR_UNSUPPORTED, "65535");
+    expect("pad+rope too many tasks", dit_pad_tokens_rope(a, b, 1, 10, 1 << 24, 3, 24, 128, 2, t, t, nullptr), DIT_ERR_UNSUPPORTED, "2^31");
+    expect("pad+rope empty", dit_pad_tokens_rope(nullptr, nullptr, 1, 0, 0, 3, 2, 128, 2, nullptr, nullptr, nullptr), DIT_OK, nullptr);
+  }
   expect("unpad alias", dit_unpad_tokens(a, a, 1, 10, 5, 256, nullptr), DIT_ERR_INVALID, "alias");
   expect("unpad NULL", dit_unpad_tokens(nullptr, b, 1, 10, 5, 256, nullptr), DIT_ERR_INVALID, "non-NULL");
   int s_pad = 0;

@@ -26,7 +26,8 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     names = header_functions()
-    for want in ("dit_attn_fwd", "dit_lse_merge", "dit_rope_split_tables", "dit_pad_tokens", "dit_unpad_tokens"):
+    for want in ("dit_attn_fwd", "dit_lse_merge", "dit_rope_split_tables", "dit_pad_tokens", "dit_pad_tokens_rope",
+                 "dit_unpad_tokens"):
         assert want in names
 
 
@@ -132,3 +133,21 @@ def test_merge_tables_pad_reject_bad_arguments(L):
     assert L.dit_pad_tokens(vp(0x1000), vp(0x2000), 1, 10, 5, 256, None) == -1
     assert L.dit_unpad_tokens(vp(0x1000), vp(0x1000), 1, 10, 5, 256, None) == -1
     assert L.dit_pad_tokens(vp(0x1000), vp(0x2000), 1, 10, 16, 0, None) == -1
+    # fused pad + rotation: shape, d, alias, tables, alignment and size checks
+    t = vp(0x30000000)
+    rope = L.dit_pad_tokens_rope
+    assert rope(vp(0x1000), vp(0x2000), 1, 10, 5, 3, 2, 128, 2, t, t, None) == -1
+    assert rope(vp(0x1000), vp(0x2000), 1, 10, 16, 3, 2, 128, 4, t, t, None) == -1
+    assert b"n_rot" in L.dit_last_error()
+    assert rope(vp(0x1000), vp(0x2000), 1, 10, 16, 0, 2, 128, 0, t, t, None) == -1
+    assert rope(vp(0x1000), vp(0x2000), 1, 10, 16, 3, 2, 96, 2, t, t, None) == -2
+    assert rope(vp(0x1000), vp(0x1000), 1, 10, 16, 3, 2, 128, 2, t, t, None) == -1
+    assert b"alias" in L.dit_last_error()
+    assert rope(vp(0x1000), vp(0x2000), 1, 10, 16, 3, 2, 128, 2, None, t, None) == -1
+    assert b"cos_t" in L.dit_last_error()
+    assert rope(vp(0x1008), vp(0x2000), 1, 10, 16, 3, 2, 128, 2, t, t, None) == -1
+    assert b"16-byte" in L.dit_last_error()
+    assert rope(vp(0x1000), vp(0x2000), 70000, 10, 16, 3, 2, 128, 2, t, t, None) == -2
+    assert rope(vp(0x1000), vp(0x2000), 1, 10, 1 << 24, 3, 24, 128, 2, t, t, None) == -2
+    assert b"2^31" in L.dit_last_error()
+    assert rope(None, None, 1, 0, 0, 3, 2, 128, 2, None, None, None) == 0   # nothing to do, no launch

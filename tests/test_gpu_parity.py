@@ -955,6 +955,104 @@ def test_pad_unpad_round_trip(ops):
         assert np.array_equal(to_np_f64(p), ref)
 
 
+@pytest.mark.parametrize("case", [
+    dict(B=1, s_valid=300, s_pad=320, T=3, H=2, d=64, n_rot=2, seed=51),
+    dict(B=2, s_valid=37, s_pad=48, T=3, H=3, d=128, n_rot=2, seed=52),
+    dict(B=1, s_valid=130, s_pad=256, T=2, H=5, d=128, n_rot=1, seed=53),
+    dict(B=1, s_valid=64, s_pad=64, T=3, H=1, d=64, n_rot=3, seed=54),
+    dict(B=1, s_valid=20, s_pad=32, T=3, H=2, d=128, n_rot=0, seed=55),
+    dict(B=1, s_valid=0, s_pad=16, T=3, H=2, d=128, n_rot=2, seed=56),
+])
+def test_pad_tokens_rope_against_oracle(ops, case):
+    """dit_pad_tokens_rope against the oracle's pad followed by its
+    split-halves rotation of the first n_rot tensors (fp64, from the same
+    bf16 inputs and fp32 tables): the other tensors and the zero pad rows are
+    bit-exact; a rotated value is the bf16 rounding of the fp32 computation,
+    so it lies within half a bf16 ulp of itself plus the fp32 error of one
+    product and one fma, 2^-23 (|x1 c| + |x2 s|), of the exact rotation."""
+    import torch
+    c = case
+    say(f"pad_tokens_rope {c}")
+    r = np.random.default_rng(c["seed"])
+    B, Sv, Sp, T, H, d, nr = c["B"], c["s_valid"], c["s_pad"], c["T"], c["H"], c["d"], c["n_rot"]
+    x = W.bf16_bits((r.standard_normal((B, Sv, T, H, d)) * 2.0).astype(np.float32))
+    pos = r.integers(0, 60, size=(Sp, 3)).astype(np.int32)
+    axes = [d // 2, d // 4, d // 4]   # t, h, w channel counts
+    cos, sin = ops.rope_split_tables(torch.from_numpy(pos).to(dev()), axes, d, 10000.0)
+    out = ops.pad_tokens_rope(to_dev_bf16(x), Sp, cos, sin, n_rot=nr)
+    torch.cuda.synchronize()
+    got_bits = raw_bits(out)
+    got = to_np_f64(out)
+    xf = oracle.bf16_to_f64(x)
+    ref = oracle.pad_tokens(xf, Sp)                             # [B, Sp, T, H, d]
+    cf, sf = to_np_f64(cos)[:Sv], to_np_f64(sin)[:Sv]
+    if nr > 0 and Sv > 0:
+        xr = np.moveaxis(xf[:, :, :nr], 1, 3)                   # [B, nr, H, Sv, d]
+        rot = np.moveaxis(oracle.rope_split_halves(xr, cf, sf), 3, 1)
+        ref[:, :Sv, :nr] = rot
+        h = d // 2
+        x1, x2 = np.abs(xf[:, :, :nr, :, :h]), np.abs(xf[:, :, :nr, :, h:])
+        ca, sa = np.abs(cf)[None, :, None, None, :], np.abs(sf)[None, :, None, None, :]
+        mag = x1 * ca + x2 * sa
+        err_f32 = 2.0 ** -23 * np.concatenate([mag, mag], axis=-1)
+        g = got[:, :Sv, :nr]
+        ulp = np.where(g == 0, 0.0, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(g), 1e-300))) - 7))
+        excess = np.abs(g - rot) - (0.5 * ulp + err_f32)
+        assert excess.max() <= 0, f"rotated value off by {excess.max()} beyond the bound"
+        # almost every value is the correctly rounded one
+        exact = W.bf16_bits(rot.astype(np.float32))
+        agree = np.mean(got_bits[:, :Sv, :nr] == exact.view(np.int16))
+        assert agree > 0.999, agree
+    # copied tensors and pad rows: bit-exact
+    assert np.array_equal(got_bits[:, :Sv, nr:], x[:, :, nr:].view(np.int16))
+    assert (got_bits[:, Sv:] == 0).all()
+
+
+def test_fused_pad_rope_step_equals_pad_then_call(ops):
+    """The Wan 480p step with the rotation fused into the pad
+    (dit_pad_tokens_rope, then dit_attn_fwd without tables) gives the same
+    O and LSE bits as the pad followed by dit_attn_fwd with the tables (its
+    own pre-pass), and the padded Q/K equal the pre-pass's rotated copies."""
+    import torch
+    w = W.WORKLOADS["wan480"]
+    say("fused pad + rope step vs pad + call with tables (wan480)")
+    B, H, d, Sv, Sp = w.B, w.H, w.d, w.s_valid, w.s_pad
+    q, k, v = W.make_qkv(w)
+    tok = lambda x: np.ascontiguousarray(x[:, :, :Sv].transpose(0, 2, 1, 3))
+    qkv_tok = to_dev_bf16(np.stack([tok(q), tok(k), tok(v)], axis=2))
+    cos, sin = gpu_tables(ops, w)
+    lse_a = torch.empty((B, H, Sp), dtype=torch.float32, device=dev())
+    lse_b = torch.empty_like(lse_a)
+    op_a = torch.empty((B, Sp, H, d), dtype=torch.bfloat16, device=dev())
+    op_b = torch.empty_like(op_a)
+    # (a) pad, then the call rotates Q and K in its pre-pass
+    qkvp = ops.pad_tokens(qkv_tok, Sp)
+    qa, ka, va = (qkvp[:, :, i].transpose(1, 2) for i in range(3))
+    ws = torch.empty(ops.attn_workspace_size(qa, ka, va, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin),
+                                             rope_k=(cos, sin)), dtype=torch.uint8, device=dev())
+    ops.attn_fwd(qa, ka, va, q_valid=Sv, kv_valid=Sv, rope_q=(cos, sin), rope_k=(cos, sin),
+                 out=op_a.transpose(1, 2), lse=lse_a, workspace=ws)
+    torch.cuda.synchronize()
+    n_el = B * H * Sp * d
+    k_rot = ws[: n_el * 2].view(torch.bfloat16).view(B, H, Sp, d).clone()
+    q_rot = ws[n_el * 2: n_el * 4].view(torch.bfloat16).view(B, H, Sp, d).clone()
+    # (b) pad with the rotation fused, then the call without tables
+    qkvr = ops.pad_tokens_rope(qkv_tok, Sp, cos, sin, n_rot=2)
+    qb, kb, vb = (qkvr[:, :, i].transpose(1, 2) for i in range(3))
+    ops.attn_fwd(qb, kb, vb, q_valid=Sv, kv_valid=Sv, out=op_b.transpose(1, 2), lse=lse_b)
+    torch.cuda.synchronize()
+    assert torch.equal(raw_bits_t(qb[:, :, :Sv]), raw_bits_t(q_rot[:, :, :Sv]))
+    assert torch.equal(raw_bits_t(kb[:, :, :Sv]), raw_bits_t(k_rot[:, :, :Sv]))
+    assert torch.equal(raw_bits_t(vb), raw_bits_t(va))
+    assert torch.equal(op_a.view(torch.int16), op_b.view(torch.int16))
+    assert torch.equal(lse_a, lse_b)
+
+
+def raw_bits_t(t):
+    import torch
+    return t.contiguous().view(torch.int16)
+
+
 # ------------------------------------------------------------------ schedules
 @pytest.mark.parametrize("case", [
     dict(name="tiny", sched=2),
