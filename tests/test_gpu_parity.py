@@ -1008,6 +1008,41 @@ def test_pad_tokens_rope_against_oracle(ops, case):
     assert (got_bits[:, Sv:] == 0).all()
 
 
+def test_pad_tokens_rope_grid_stride_sampled(ops):
+    """A pad large enough that the launch's 65535 blocks stride over the
+    rows (3 x 24 heads x d = 128 over 30000 rows: 17.3 M tasks of 256
+    threads' worth): copies and zero pad rows checked whole on the device,
+    the rotated Q/K rows checked on a sample (the first and last real rows,
+    rows around every stride boundary, random rows) against the oracle."""
+    import torch
+    say("pad_tokens_rope, grid-stride size (sampled rows)")
+    B, Sv, Sp, T, H, d = 1, 29950, 30000, 3, 24, 128
+    g = torch.Generator(device=dev()).manual_seed(57)
+    x = torch.randn((B, Sv, T, H, d), generator=g, device=dev()).mul_(2.0).to(torch.bfloat16)
+    r = np.random.default_rng(57)
+    pos = r.integers(0, 200, size=(Sp, 3)).astype(np.int32)
+    cos, sin = ops.rope_split_tables(torch.from_numpy(pos).to(dev()), [64, 32, 32], d, 10000.0)
+    out = ops.pad_tokens_rope(x, Sp, cos, sin, n_rot=2)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :Sv, 2:].view(torch.int16), x[:, :, 2:].view(torch.int16))
+    assert (out[:, Sv:].view(torch.int16) == 0).all()
+    per_row = T * H * (d // 16)
+    stride_rows = 65535 * 256 // per_row
+    rows = sorted(set([0, 1, Sv - 1, Sv - 2] + [k * stride_rows + o for k in (1, 2) for o in (-1, 0, 1)
+                                                  if 0 <= k * stride_rows + o < Sv]
+                      + list(r.integers(0, Sv, 24))))
+    idx = torch.tensor(rows, device=dev())
+    xs = to_np_f64(x[0, idx, :2])                               # [n, 2, H, d]
+    gs = to_np_f64(out[0, idx, :2])
+    cf, sf = to_np_f64(cos[idx]), to_np_f64(sin[idx])
+    ref = np.moveaxis(oracle.rope_split_halves(np.moveaxis(xs, 0, 2), cf, sf), 2, 0)
+    h = d // 2
+    mag = np.abs(xs[..., :h]) * np.abs(cf)[:, None, None, :] + np.abs(xs[..., h:]) * np.abs(sf)[:, None, None, :]
+    err_f32 = 2.0 ** -23 * np.concatenate([mag, mag], axis=-1)
+    ulp = np.where(gs == 0, 0.0, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(gs), 1e-300))) - 7))
+    assert (np.abs(gs - ref) - (0.5 * ulp + err_f32)).max() <= 0
+
+
 def test_fused_pad_rope_step_equals_pad_then_call(ops):
     """The Wan 480p step with the rotation fused into the pad
     (dit_pad_tokens_rope, then dit_attn_fwd without tables) gives the same
