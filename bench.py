@@ -435,8 +435,8 @@ def pmc_target(args):
 def hbm_passes(args):
     """The HBM-bound passes on Wan 720p-sized buffers (larger than the 256 MB
     MALL, so the figures are HBM rates): pad and unpad of one token-major
-    tensor [1, S, 10, 128] bf16, the 4-part fp32 -> bf16 LSE merge, and the
-    RoPE tables. Prints one JSON line of average µs and GB/s per pass (HIP
+    tensor [1, S, 10, 128] bf16, the pad of the fused Q/K/V rows with Q and K
+    rotated, the 4-part fp32 -> bf16 LSE merge, and the RoPE tables. Prints one JSON line of average µs and GB/s per pass (HIP
     events over 20 back-to-back calls after 5 warm-up calls); run under
     rocprofv3 --kernel-trace for the per-kernel durations."""
     import torch
@@ -465,9 +465,15 @@ def hbm_passes(args):
                      dtype=torch.uint8, device=dev)
     groups = -(-H // 4)
     prepass_bytes = (Sp + Sv) * row * 2 + (Sp + Sv) * groups * d * 4
+    # the fused Q/K/V pad with Q and K rotated on the way: rows read and
+    # written, plus the fp32 tables once per real row
+    qkv = torch.randn((1, Sv, 3, H, d), device=dev).to(torch.bfloat16)
+    qkvp = torch.empty((1, Sp, 3, H, d), dtype=torch.bfloat16, device=dev)
     res = {}
     for name, fn, nbytes in (
             ("pad_tokens", lambda: ops.pad_tokens(x, Sp, out=xp), (Sv + Sp) * row),
+            ("pad_tokens_rope(fused QKV, Q/K rotated)", lambda: ops.pad_tokens_rope(qkv, Sp, cos, sin, n_rot=2, out=qkvp),
+             (Sv + Sp) * 3 * row + Sv * d * 4),
             ("unpad_tokens", lambda: ops.unpad_tokens(xp, Sv, out=xu), 2 * Sv * row),
             ("lse_merge_4xf32_to_bf16", lambda: ops.lse_merge(parts_o, parts_l, q_valid=Sv, out=om, lse_out=lm),
              4 * H * Sp * (d * 4 + 4) + H * Sp * (d * 2 + 4)),

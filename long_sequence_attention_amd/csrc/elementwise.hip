@@ -131,9 +131,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
 // writes whole rows. Head vectors of the first n_rot tensors of a real row are
 // rotated with that row's tables by rotate8, the routine of the attention
 // pre-pass, so the two paths give the same bits; the others are copied; pad
-// rows are written as zeros. (T * H * RUNS * s_pad < 2^31 is checked by the
-// caller, so the task index is 32-bit.)
-template <int RUNS>
+// rows are written as zeros. STREAM: the source rows are read with
+// non-temporal loads (copies larger than the MALL, as in row_copy_kernel).
+// (T * H * RUNS * s_pad < 2^31 is checked by the caller, so the task index
+// is 32-bit.)
+template <int RUNS, bool STREAM>
 __global__ __launch_bounds__(256) void pad_rope_kernel(PadRopeParams p) {
   constexpr int HALF = RUNS * 8;
   const uint32_t vecs = (uint32_t)(p.T * p.H);
@@ -150,8 +152,10 @@ __global__ __launch_bounds__(256) void pad_rope_kernel(PadRopeParams p) {
     const int64_t off = (int64_t)s * row_elems + (int64_t)vec * (2 * HALF) + c * 8;
     u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
     if (s < (uint32_t)p.s_valid) {
-      lo = *reinterpret_cast<const u32x4 *>(src + off);
-      hi = *reinterpret_cast<const u32x4 *>(src + off + HALF);
+      const u32x4 *a = reinterpret_cast<const u32x4 *>(src + off);
+      const u32x4 *b = reinterpret_cast<const u32x4 *>(src + off + HALF);
+      lo = STREAM ? __builtin_nontemporal_load(a) : *a;
+      hi = STREAM ? __builtin_nontemporal_load(b) : *b;
       if (vec < n_rot_vecs) {
         float cv[8], sv[8], x1[8], x2[8];
         load8f(p.cos_t + (int64_t)s * HALF + c * 8, cv);
@@ -227,8 +231,16 @@ hipError_t launch_pad_rope(const PadRopeParams &p, int B, int d, hipStream_t str
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65535) blocks = 65535;   // the kernel strides over the rest
   const dim3 grid((unsigned)blocks, (unsigned)B);
-  if (d == 128) hipLaunchKernelGGL(pad_rope_kernel<8>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(pad_rope_kernel<4>, grid, dim3(256), 0, stream, p);
+  // the same size rule as the row copies: reads and writes together beyond
+  // 128 MB take the non-temporal source loads
+  const bool large = (int64_t)B * total * 32 * 2 > (128LL << 20);
+  if (d == 128) {
+    if (large) hipLaunchKernelGGL((pad_rope_kernel<8, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((pad_rope_kernel<8, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (large) hipLaunchKernelGGL((pad_rope_kernel<4, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((pad_rope_kernel<4, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
