@@ -396,10 +396,10 @@ def test_fixed_m_falls_back_to_online_for_a_loose_bound(ops):
     assert np.array_equal(raw_bits(o1), raw_bits(o0)) and np.array_equal(raw_bits(l1), raw_bits(l0))
 
 
-def _random_case(seed):
+def _random_case(seed, max_len=700):
     r = np.random.default_rng(seed)
     d = int(r.choice([64, 128]))
-    s_q, s_kv = int(r.integers(1, 700)), int(r.integers(1, 700))
+    s_q, s_kv = int(r.integers(1, max_len)), int(r.integers(1, max_len))
     c = dict(B=int(r.integers(1, 3)), H=int(r.integers(1, 5)), d=d, s_q=s_q, s_kv=s_kv,
              q_valid=int(r.integers(0, s_q + 1)), kv_valid=int(r.integers(0, s_kv + 1)),
              rope_q=bool(r.random() < 0.6), rope_k=bool(r.random() < 0.6), norm=bool(r.random() < 0.3),
@@ -417,8 +417,20 @@ def test_random_shapes_against_oracle(ops, seed):
     oracle: O within the derived rounding bound of the oracle on the
     bf16-rounded prepared Q/K, LSE within the derived bound of the unrounded
     oracle, pad rows 0 / -inf."""
+    _check_random_case(ops, seed, _random_case(seed))
+
+
+@pytest.mark.parametrize("seed", list(range(200, 212)))
+def test_random_larger_shapes_against_oracle(ops, seed):
+    """The same checks on lengths up to 3000 rows (up to 12 q-tiles and 47
+    key tiles per head): several q-tiles per head under every schedule,
+    split pieces that span q-tile boundaries, dynamic placement with spare
+    workgroups."""
+    _check_random_case(ops, seed, _random_case(seed, max_len=3000))
+
+
+def _check_random_case(ops, seed, c):
     import torch
-    c = _random_case(seed)
     say(f"random {seed}: {c}")
     r = np.random.default_rng(1000 + seed)
     B, H, d, s_q, s_kv = c["B"], c["H"], c["d"], c["s_q"], c["s_kv"]
