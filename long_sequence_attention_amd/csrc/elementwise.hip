@@ -30,6 +30,33 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(TableParams p) {
   }
 }
 
+// The same tables, PER consecutive pairs of one row per thread (used when
+// half_d is a multiple of PER and the outputs are 16-byte aligned): the PER
+// angles are independent, so their fp64 cos/sin overlap, and each output
+// leaves as one PER x 4-byte store. Same arithmetic per entry, same bits.
+template <int PER>
+__global__ __launch_bounds__(256) void rope_tables_vec_kernel(TableParams p) {
+  typedef float fvec __attribute__((ext_vector_type(PER)));
+  const int per_row = p.half_d / PER;
+  const int total = p.S * per_row;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < total; t += gridDim.x * blockDim.x) {
+    const int s = t / per_row;
+    const int j0 = (t - s * per_row) * PER;
+    const int32_t *ps = p.pos + (int64_t)s * p.n_axes;
+    fvec cv, sv;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const double ang = (double)ps[p.axis[j0 + e]] * p.freq[j0 + e];
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      cv[e] = (float)cs;
+      sv[e] = (float)sn;
+    }
+    *reinterpret_cast<fvec *>(p.cos_out + (int64_t)s * p.half_d + j0) = cv;
+    *reinterpret_cast<fvec *>(p.sin_out + (int64_t)s * p.half_d + j0) = sv;
+  }
+}
+
 // Tail pad / unpad of one batch (blockIdx.y): rows 0..n_copy-1 of both
 // sides are one contiguous run, so out[i] = in[i] for i < n_copy granules
 // and out[i] = 0 up to n_total. V is the copy granule (16, 4 or 1 bytes),
@@ -183,7 +210,11 @@ int grid_for(int64_t total) {
 hipError_t launch_rope_tables(const TableParams &p, hipStream_t stream) {
   const int64_t total = (int64_t)p.S * p.half_d;
   if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_tables_kernel, dim3(grid_for(total)), dim3(256), 0, stream, p);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(p.cos_out) | reinterpret_cast<uintptr_t>(p.sin_out);
+  if (p.half_d % 4 == 0 && al % 16 == 0)
+    hipLaunchKernelGGL(rope_tables_vec_kernel<4>, dim3(grid_for(total / 4)), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(rope_tables_kernel, dim3(grid_for(total)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
